@@ -1,0 +1,181 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD forward pass.
+ *
+ * The operation (per sequence s and head h, group g = h / (nheads/ngroups)):
+ *
+ *   state <- initial_state[s, h]  (headdim x dstate, fp32), or zeros
+ *   for each token t of s:
+ *     state[p, n] = exp(dt[t, h] * A[h]) * state[p, n] + dt[t, h] * x[t, h, p] * B[t, g, n]
+ *     y[t, h, p]  = sum_n C[t, g, n] * state[p, n] + D[h] * x[t, h, p]
+ *   final_state[s, h] <- state
+ *
+ * Sources: the selective SSM with per-token step size, B and C and the decay
+ * exp(step * A) (tj-hxxt.cn long read of "Mamba: Linear-Time Sequence Modeling
+ * with Selective State Spaces", part III, sub-sections (2) and 3); the
+ * equivalence of this recurrence with a masked-attention product by a
+ * semiseparable matrix, and its evaluation by block-decomposed matrix products
+ * (QbitAI "Mamba-2" article, srwj168 repost, sections "Unifying SSM and
+ * attention" and "Mamba-2: stronger learning, faster training and inference",
+ * which also names variable sequence lengths); the state reset between packed
+ * sequences (same long read, part III item 2.3 "Boundary Resetting").
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or synchronises; ssd_forward only enqueues kernels
+ *    on the given HIP stream and returns.
+ *  - Tensors are dense, row-major (C-contiguous) in the shapes listed, with
+ *    the token index flattened as t = b * seqlen + l (dense batch) or the
+ *    packed position (varlen). Every pointer must be 16-byte aligned.
+ *  - x, dt, B, C and y share one element type (ssd_dtype). A, D, the initial
+ *    and final states and all internal states are fp32; accumulation is fp32.
+ *  - Errors are reported by return code; no exception crosses the ABI.
+ *    Argument errors are detected before anything is enqueued. A thread-local
+ *    message with details is available from ssd_last_error_detail().
+ *  - The library keeps no state between calls and is safe to call from
+ *    several host threads at once (on different workspaces).
+ */
+#ifndef SSD_MI355X_H_
+#define SSD_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1, /* malformed shape, pointer, size or cu_seqlens */
+  SSD_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported set */
+  SSD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  SSD_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} ssd_status;
+
+typedef enum ssd_dtype {
+  SSD_DTYPE_F32 = 0,  /* IEEE fp32 */
+  SSD_DTYPE_BF16 = 1  /* bfloat16; y rounded to nearest even */
+} ssd_dtype;
+
+/* Flags for ssd_problem.flags. */
+#define SSD_FLAG_GENERIC_KERNELS 1u /* use the plain FMA kernels even where the
+                                       MFMA kernels apply (testing aid) */
+
+/*
+ * Problem description.
+ *   batch      dense batch rows (>= 1); must be 1 in varlen mode
+ *   seqlen     tokens per batch row; in varlen mode the total packed tokens
+ *   nheads     H >= 1
+ *   headdim    P: 16, 32, 64 or 128
+ *   dstate     N: a multiple of 16, 16 <= N <= 256
+ *   ngroups    G >= 1 with H % G == 0; head h reads B and C of group
+ *              h / (H / G), so consecutive heads share a group
+ *   chunk_size Q: 64, 128 or 256 (the result does not depend on Q beyond
+ *              rounding)
+ *   num_seqs   0 = dense batch; > 0 = varlen with that many packed sequences
+ *   dtype      ssd_dtype of x, dt, B, C, y
+ *   flags      0 or SSD_FLAG_* bits
+ */
+typedef struct ssd_problem {
+  int32_t batch;
+  int32_t seqlen;
+  int32_t nheads;
+  int32_t headdim;
+  int32_t dstate;
+  int32_t ngroups;
+  int32_t chunk_size;
+  int32_t num_seqs;
+  int32_t dtype;
+  uint32_t flags;
+} ssd_problem;
+
+/* Check a problem description (host only, no device access).
+ * Returns SSD_OK, SSD_ERR_INVALID_ARG (null, non-positive or inconsistent
+ * sizes, H % G != 0, batch != 1 with num_seqs > 0, sizes whose element
+ * counts overflow int32 indexing) or SSD_ERR_UNSUPPORTED (headdim, dstate,
+ * chunk_size or dtype outside the supported set). */
+ssd_status ssd_validate(const ssd_problem *prob);
+
+/* Check host-resident cu_seqlens (num_seqs + 1 int32 values) against a
+ * varlen problem: cu[0] == 0, non-decreasing, cu[num_seqs] == seqlen.
+ * Zero-length sequences are allowed (their final state is their initial
+ * state). Host only. */
+ssd_status ssd_validate_cu_seqlens(const ssd_problem *prob,
+                                   const int32_t *host_cu_seqlens);
+
+/* Bytes of device workspace ssd_forward needs for this problem (host only).
+ * The size depends only on the problem (never on the cu_seqlens values):
+ * fp32 per-chunk states (chunks x H x P x N), per-chunk decay prefixes
+ * (chunks x H x Q) and the chunk table, where chunks = batch * ceil(seqlen/Q)
+ * (dense) or floor(seqlen/Q) + num_seqs (varlen upper bound). */
+ssd_status ssd_workspace_size(const ssd_problem *prob, size_t *bytes);
+
+/*
+ * Run the SSD forward pass.
+ *   x              (batch, seqlen, H, P)     dtype
+ *   dt             (batch, seqlen, H)        dtype; step sizes as given
+ *                                            (already positive; no bias,
+ *                                            softplus or clamp applied here)
+ *   A              (H)                       fp32 (decay exp(dt*A); A <= 0
+ *                                            expected, not required)
+ *   B, C           (batch, seqlen, G, N)     dtype
+ *   D              (H)                       fp32, NULL = no skip term
+ *   initial_state  (batch | num_seqs, H, P, N) fp32, NULL = zeros
+ *   cu_seqlens     (num_seqs + 1)            int32 device array, varlen only
+ *                                            (NULL in dense mode). Values must
+ *                                            satisfy ssd_validate_cu_seqlens;
+ *                                            they are not read by the host.
+ *                                            Invalid device values never
+ *                                            cause an out-of-bounds access,
+ *                                            but y and final_state are then
+ *                                            unspecified.
+ *   y              (batch, seqlen, H, P)     dtype, written (out)
+ *   final_state    (batch | num_seqs, H, P, N) fp32 (out), NULL = not written
+ *   workspace      device buffer of at least ssd_workspace_size() bytes,
+ *                  256-byte aligned; its contents on entry do not matter
+ *   stream         a hipStream_t (NULL = the default stream)
+ * Inputs and outputs must not overlap. Returns SSD_OK once all kernels are
+ * enqueued; SSD_ERR_HIP if a launch fails.
+ */
+ssd_status ssd_forward(const ssd_problem *prob, const void *x, const void *dt,
+                       const float *A, const void *B, const void *C,
+                       const float *D, const float *initial_state,
+                       const int32_t *cu_seqlens, void *y, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Where ssd_forward leaves its intermediates inside the workspace (byte
+ * offsets), for inspection after the stream has completed:
+ *   chunk_cumsum  fp32 (chunks, H, Q): inclusive prefix of dt*A*log2(e)
+ *                 inside each chunk, i.e. the base-2 logarithm of the decay
+ *                 from the chunk's start through each token (entries past a
+ *                 partial chunk's end are unspecified)
+ *   chunk_states  fp32 (chunks, H, P, N): the state entering each chunk
+ *   chunk_table   int32 (varlen only): [0] = number of chunks, [1] = nonzero
+ *                 if the device cu_seqlens were invalid, [2 .. num_seqs+2] =
+ *                 first chunk of each sequence followed by the total, then
+ *                 from int offset chunk_records one (sequence, first token,
+ *                 length, index in sequence) record per chunk
+ *   chunk_records int32 offset of the records inside chunk_table
+ *   max_chunks    chunks the layout has room for
+ * Host only. */
+typedef struct ssd_workspace_layout {
+  size_t chunk_cumsum;
+  size_t chunk_states;
+  size_t chunk_table;
+  int64_t chunk_records;
+  int64_t max_chunks;
+} ssd_workspace_layout;
+ssd_status ssd_get_workspace_layout(const ssd_problem *prob,
+                                    ssd_workspace_layout *layout);
+
+/* Static text for a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *ssd_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H_ */

@@ -1,0 +1,15 @@
+"""Mamba-2 SSD forward pass for AMD Instinct MI355X (gfx950).
+
+The hot path is the C-ABI library ``libssd.so`` (HIP kernels, declared in
+``include/ssd.h``); this package is its thin Python binding. Build the library
+with ``python -m mamba_ssd_sequence_fwd_amd.build``.
+
+    y, final_state = forward(x, dt, A, B, C, D, initial_state, chunk_size=256,
+                             cu_seqlens=None)
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED, LIB_PATH, Plan, Problem, SSDError, WorkspaceLayout, forward, load,
+    make_problem, validate, validate_cu_seqlens, workspace_layout, workspace_size,
+    SSD_DTYPE_BF16, SSD_DTYPE_F32, SSD_FLAG_GENERIC_KERNELS, SSD_OK,
+    SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP,
+)

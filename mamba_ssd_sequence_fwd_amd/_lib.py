@@ -1,0 +1,210 @@
+"""ctypes binding of ``libssd.so`` (declared in ``include/ssd.h``).
+
+Argument marshalling only: torch provides device memory and the current HIP
+stream; every step of the SSD forward pass runs in the library's kernels.
+There is no CPU fallback -- if the library is missing, import succeeds but
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
+SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
+SSD_FLAG_GENERIC_KERNELS = 1
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, _status_string(status), detail))
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("ngroups", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return "Problem(%s)" % ", ".join("%s=%s" % (f, getattr(self, f)) for f, _ in self._fields_)
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [("chunk_cumsum", ctypes.c_size_t), ("chunk_states", ctypes.c_size_t),
+                ("chunk_table", ctypes.c_size_t), ("chunk_records", ctypes.c_int64),
+                ("max_chunks", ctypes.c_int64)]
+
+
+EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
+            "ssd_forward", "ssd_get_workspace_layout", "ssd_status_string",
+            "ssd_last_error_detail")
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libssd.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                "libssd.so is not built (%s); run `python -m mamba_ssd_sequence_fwd_amd.build`"
+                % path)
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER(Problem)
+        vp = ctypes.c_void_p
+        lib.ssd_validate.argtypes = [P]
+        lib.ssd_validate_cu_seqlens.argtypes = [P, vp]
+        lib.ssd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssd_get_workspace_layout.argtypes = [P, ctypes.POINTER(WorkspaceLayout)]
+        lib.ssd_forward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
+        for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
+                  "ssd_get_workspace_layout", "ssd_forward"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.ssd_status_string.argtypes = [ctypes.c_int]
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_last_error_detail.argtypes = []
+        lib.ssd_last_error_detail.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _status_string(st: int) -> str:
+    try:
+        return load().ssd_status_string(st).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "status %d" % st
+
+
+def _check(st: int, where: str):
+    if st != SSD_OK:
+        raise SSDError(st, where, load().ssd_last_error_detail().decode())
+
+
+def make_problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
+                 num_seqs=0, dtype=SSD_DTYPE_BF16, flags=0) -> Problem:
+    return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size,
+                   num_seqs, dtype, flags)
+
+
+def validate(prob: Problem):
+    _check(load().ssd_validate(ctypes.byref(prob)), "ssd_validate")
+
+
+def validate_cu_seqlens(prob: Problem, cu_host):
+    cu = torch.as_tensor(cu_host, dtype=torch.int32).contiguous().cpu()
+    _check(load().ssd_validate_cu_seqlens(ctypes.byref(prob), ctypes.c_void_p(cu.data_ptr())),
+           "ssd_validate_cu_seqlens")
+
+
+def workspace_size(prob: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().ssd_workspace_size(ctypes.byref(prob), ctypes.byref(n)), "ssd_workspace_size")
+    return int(n.value)
+
+
+def workspace_layout(prob: Problem) -> WorkspaceLayout:
+    lay = WorkspaceLayout()
+    _check(load().ssd_get_workspace_layout(ctypes.byref(prob), ctypes.byref(lay)),
+           "ssd_get_workspace_layout")
+    return lay
+
+
+_DTYPES = {torch.bfloat16: SSD_DTYPE_BF16, torch.float32: SSD_DTYPE_F32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """A prepared ssd_forward call: validated problem, outputs and workspace
+    allocated once; :meth:`run` only enqueues the kernels.
+
+    Shapes: x (batch, L, H, P); dt (batch, L, H); A (H,) fp32; B, C
+    (batch, L, G, N); D (H,) fp32 or None; initial_state (batch | num_seqs,
+    H, P, N) fp32 or None; cu_seqlens (num_seqs + 1,) int32 (CPU or GPU) or
+    None. x, dt, B, C share the dtype (bfloat16 or float32).
+    """
+
+    def __init__(self, x, dt, A, B, C, D=None, initial_state=None, chunk_size=256,
+                 cu_seqlens=None, *, want_final_state=True, generic=False,
+                 check_cu_seqlens=True):
+        if x.dim() != 4:
+            raise ValueError("x must be (batch, seqlen, nheads, headdim)")
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        dev = x.device
+        if dev.type != "cuda":
+            raise ValueError("tensors must be on the GPU (got %s)" % dev)
+        if x.dtype not in _DTYPES:
+            raise ValueError("x must be bfloat16 or float32")
+        for name, t, shape in (("dt", dt, (batch, L, H)), ("B", B, (batch, L, G, N)),
+                               ("C", C, (batch, L, G, N))):
+            if tuple(t.shape) != shape or t.dtype != x.dtype or t.device != dev:
+                raise ValueError("%s must be %s %s on %s" % (name, shape, x.dtype, dev))
+        if tuple(A.shape) != (H,) or A.dtype != torch.float32:
+            raise ValueError("A must be (H,) float32")
+        if D is not None and (tuple(D.shape) != (H,) or D.dtype != torch.float32):
+            raise ValueError("D must be (H,) float32")
+        num_seqs = 0
+        cu_dev = None
+        if cu_seqlens is not None:
+            if batch != 1:
+                raise ValueError("cu_seqlens needs batch == 1")
+            num_seqs = int(cu_seqlens.numel()) - 1
+        nstate = num_seqs if num_seqs else batch
+        if initial_state is not None and (
+                tuple(initial_state.shape) != (nstate, H, P, N)
+                or initial_state.dtype != torch.float32):
+            raise ValueError("initial_state must be (%d, %d, %d, %d) float32" % (nstate, H, P, N))
+        self.prob = make_problem(batch, L, H, P, N, G, chunk_size, num_seqs,
+                                 _DTYPES[x.dtype],
+                                 SSD_FLAG_GENERIC_KERNELS if generic else 0)
+        validate(self.prob)
+        if cu_seqlens is not None:
+            if check_cu_seqlens or cu_seqlens.device.type == "cpu":
+                validate_cu_seqlens(self.prob, cu_seqlens.detach().cpu())
+            cu_dev = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        self.inputs = [t.contiguous() if t is not None else None
+                       for t in (x, dt, A, B, C, D, initial_state)]
+        self.cu = cu_dev
+        self.y = torch.empty_like(x)
+        self.final_state = (torch.empty((nstate, H, P, N), device=dev, dtype=torch.float32)
+                            if want_final_state else None)
+        self.ws_bytes = workspace_size(self.prob)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), device=dev, dtype=torch.uint8)
+        self.tokens = batch * L
+
+    def run(self, stream=None):
+        """Enqueue one forward pass on ``stream`` (default: torch's current)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.y.device)
+        x, dt, A, B, C, D, h0 = self.inputs
+        _check(load().ssd_forward(
+            ctypes.byref(self.prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(h0), _ptr(self.cu), _ptr(self.y), _ptr(self.final_state),
+            _ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()),
+            ctypes.c_void_p(stream.cuda_stream)), "ssd_forward")
+        return self.y, self.final_state
+
+    def layout(self) -> WorkspaceLayout:
+        return workspace_layout(self.prob)
+
+
+def forward(x, dt, A, B, C, D=None, initial_state=None, chunk_size=256, cu_seqlens=None,
+            **kw):
+    """SSD forward pass: returns (y, final_state)."""
+    return Plan(x, dt, A, B, C, D, initial_state, chunk_size, cu_seqlens, **kw).run()

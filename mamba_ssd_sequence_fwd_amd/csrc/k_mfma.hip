@@ -1,0 +1,431 @@
+// k_mfma.hip -- bf16 MFMA kernels of the chunked SSD forward pass (gfx950).
+//
+// The SSD layer multiplies the sequence by a semiseparable matrix; cut into
+// chunks of Q tokens, the diagonal blocks are masked-attention products
+// (C B^T, masked by the decay matrix, times x) and the off-diagonal blocks
+// factor through one state per chunk (QbitAI "Mamba-2" article, srwj168
+// repost, sections "Unifying SSM and attention" and "Mamba-2: stronger
+// learning, faster training and inference"; C, B, x play query, key, value:
+// kuaisou "mamba model explained" snippets). Three kernels here:
+//
+//   k_chunk_state_mfma (row a3): S_c = (w o X_c)^T B_c, w_s = 2^(cs_last-cs_s) dt_s.
+//   k_chunk_cb         (row a5, part 1): C_c B_c^T once per (chunk, group),
+//                      lower-triangular 32x32 tiles only, stored in bf16 in the
+//                      exact register layout chunk_scan feeds to the MFMA.
+//   k_chunk_scan_mfma  (row a5, part 2): y = 2^(cs_l) C h_prev^T
+//                      + (CB o decay mask) (dt o X) + D x.
+//
+// MFMA used: v_mfma_f32_16x16x32_bf16 (D 16x16 fp32 += A 16x32 * B 32x16).
+// Lane L holds A row (L % 16), B column (L % 16), K elements
+// 8*(L/16) .. 8*(L/16)+7 of both; D column (L % 16), rows 4*(L/16) .. +3.
+// Any fixed permutation of the K slots works as long as A and B use the same
+// one; chunk_scan uses the permutation that the C B^T accumulators produce.
+//
+// Shapes: P = 64, N in {64, 128, 256}, Q in {64, 128, 256}.
+// LDS tiles are [row][col] bf16 with 16-byte chunks XOR-swizzled by (row & 7)
+// so that the 16 rows an MFMA operand read touches fall in distinct banks.
+#include "ssd_internal.h"
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kP = 64;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
+  return z;
+}
+
+// Element offset of (row, col) in a swizzled [rows][W] bf16 LDS tile.
+template <int W>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * W + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ bf16x8 ldg8(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16 a = (bf16)lo, b = (bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Stage rows [s0, s0 + 2*npairs) of a token-major bf16 matrix (row stride
+// `ld` elements, W columns used, rows >= len read as zero) into a transposed,
+// swizzled LDS tile dst[col][s - s0] (row width WT), scaling token s by
+// scale[s]. Each work item moves 2 tokens x 8 columns with two 16-byte loads
+// and eight 32-bit LDS stores (token pairs packed).
+template <int W, int WT, int NTHR>
+__device__ __forceinline__ void stage_transposed(bf16 *dst, const bf16 *src,
+                                                 size_t ld, int s0, int npairs,
+                                                 int len, const float *scale) {
+  const int items = npairs * (W / 8);
+  for (int it = threadIdx.x; it < items; it += NTHR) {
+    const int sp = it % npairs, cg = it / npairs;
+    const int s = s0 + 2 * sp;
+    bf16x8 v0 = zero8(), v1 = zero8();
+    if (s < len) v0 = ldg8(src + (size_t)s * ld + 8 * cg);
+    if (s + 1 < len) v1 = ldg8(src + (size_t)(s + 1) * ld + 8 * cg);
+    const float w0 = scale[s], w1 = scale[s + 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t pr = pack2((float)v0[e] * w0, (float)v1[e] * w1);
+      *reinterpret_cast<uint32_t *>(dst + swz<WT>(8 * cg + e, 2 * sp)) = pr;
+    }
+  }
+}
+
+// ============================================================================
+// chunk_state: S_c[p, n] = sum_s w_s x_s[p] B_s[n]
+// One workgroup (4 waves) per (chunk, head); wave w owns n in
+// [w*N/4, (w+1)*N/4) and all 64 p. Tokens go through LDS 128 at a time.
+// ============================================================================
+template <int N, int Q>
+__global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
+  constexpr int QH = Q < 128 ? Q : 128;
+  constexpr int NT = N / 64;  // 16-wide n tiles per wave
+  __shared__ __attribute__((aligned(16))) bf16 sX[kP * QH];
+  __shared__ __attribute__((aligned(16))) bf16 sB[N * QH];
+  __shared__ float sW[Q];
+  __shared__ float sOne[Q];
+  Chunk k;
+  const int c = blockIdx.x;
+  if (!chunk_of(a, c, k)) return;
+  const int h = blockIdx.y, g = h / a.heads_per_group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
+  const float last = cs[k.len - 1];
+  for (int l = tid; l < Q; l += 256) {
+    sW[l] = (l < k.len)
+                ? exp2_fast(last - cs[l]) *
+                      (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + l) * a.H + h]
+                : 0.f;
+    sOne[l] = 1.f;
+  }
+  const bf16 *xsrc = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
+  const bf16 *bsrc = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
+
+  f32x4 acc[4][NT];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[pt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = 0; s0 < Q; s0 += QH) {
+    __syncthreads();
+    stage_transposed<kP, QH, 256>(sX, xsrc, (size_t)a.H * kP, s0, QH / 2, k.len, sW);
+    stage_transposed<N, QH, 256>(sB, bsrc, (size_t)a.G * N, s0, QH / 2, k.len,
+                                 sOne);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < QH / 32; ++ks) {
+      const int col = 32 * ks + 8 * lg;
+      bf16x8 av[4], bv[NT];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+        av[pt] = *reinterpret_cast<const bf16x8 *>(sX + swz<QH>(16 * pt + lr, col));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bv[nt] = *reinterpret_cast<const bf16x8 *>(
+            sB + swz<QH>(16 * (wave * NT + nt) + lr, col));
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[pt][nt] = mfma(av[pt], bv[nt], acc[pt][nt]);
+    }
+  }
+  float *out = a.states + ((size_t)c * a.H + h) * kP * N;
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        out[(16 * pt + 4 * lg + r) * N + 16 * (wave * NT + nt) + lr] = acc[pt][nt][r];
+}
+
+// ============================================================================
+// chunk_cb: CB[l, s] = C_l . B_s for the lower-triangular 32x32 tiles (i >= j)
+// of each (chunk, group). Computed as CB^T = B C^T so that each lane ends up
+// with one row l and eight s values -- the A-operand layout of the product
+// with x in chunk_scan. Slot e of lane L holds s = 32 j + 16 (e / 4)
+// + 4 (L / 16) + (e % 4). Storage: [chunk][group][tile pair][half u][lane][8]
+// bf16, tile pair = i (i + 1) / 2 + j, half u = rows 16u..16u+15 of tile i.
+// One wave per (chunk, group, {i, T-1-i}) so every wave does T+1 tile pairs.
+// ============================================================================
+template <int N, int Q>
+__global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
+  constexpr int T = Q / 32, KS = N / 32, PAIRS = T * (T + 1) / 2;
+  Chunk k;
+  const int c = blockIdx.x;
+  if (!chunk_of(a, c, k)) return;
+  const int g = blockIdx.y, w = blockIdx.z;
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const bf16 *C = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
+  const bf16 *B = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
+  const size_t ldr = (size_t)a.G * N;
+  bf16 *base = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512;
+#pragma unroll 1
+  for (int ti = 0; ti < 2; ++ti) {
+    const int i = ti == 0 ? w : T - 1 - w;
+    bf16x8 cop[2][KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 32 * i + 16 * u + lr;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        cop[u][ks] = row < k.len ? ldg8(C + row * ldr + 32 * ks + 8 * lg) : zero8();
+    }
+#pragma unroll 1
+    for (int j = 0; j <= i; ++j) {
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int srow = 32 * j + 16 * t + lr;
+          const bf16x8 bop = srow < k.len ? ldg8(B + srow * ldr + 32 * ks + 8 * lg) : zero8();
+#pragma unroll
+          for (int u = 0; u < 2; ++u) acc[u][t] = mfma(bop, cop[u][ks], acc[u][t]);
+        }
+      }
+      const int pair = i * (i + 1) / 2 + j;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 v;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[4 * t + r] = (bf16)acc[u][t][r];
+        *reinterpret_cast<bf16x8 *>(base + (size_t)(pair * 2 + u) * 512 + lane * 8) = v;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// chunk_scan: y_l = 2^(cs_l) C_l h_prev^T + sum_{s<=l} CB[l,s] 2^(cs_l - cs_s)
+//             dt_s x_s + D x_l.
+// One workgroup per (chunk, head) with Q/64 waves; wave w owns the 32-row
+// tiles w and T-1-w (equal work per wave). (dt o x)^T and h_prev (bf16) sit in
+// LDS; C rows and the precomputed CB tiles are read straight into registers.
+// Off-diagonal tiles (j < i) split the decay at the tile's first row r0:
+// 2^(cs_l - cs_s) = 2^(cs_l - cs_r0) 2^(cs_r0 - cs_s), both factors <= 1, so
+// nothing can overflow; diagonal tiles take the exact masked exponent.
+// ============================================================================
+template <int N, int Q>
+__global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
+  constexpr int T = Q / 32, NTHR = Q, KS = N / 32, PAIRS = T * (T + 1) / 2;
+  __shared__ __attribute__((aligned(16))) bf16 sX[kP * Q];
+  __shared__ __attribute__((aligned(16))) bf16 sH[kP * N];
+  __shared__ float sCs[Q];
+  __shared__ float sDt[Q];
+  Chunk k;
+  const int c = blockIdx.x;
+  if (!chunk_of(a, c, k)) return;
+  const int h = blockIdx.y, g = h / a.heads_per_group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
+  for (int l = tid; l < Q; l += NTHR) {
+    sCs[l] = cs[min(l, k.len - 1)];
+    sDt[l] = (l < k.len) ? (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + l) * a.H + h] : 0.f;
+  }
+  __syncthreads();
+  const bf16 *xsrc = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
+  stage_transposed<kP, Q, NTHR>(sX, xsrc, (size_t)a.H * kP, 0, Q / 2, k.len, sDt);
+  {
+    const float *hp = a.states + ((size_t)c * a.H + h) * kP * N;
+    for (int it = tid; it < kP * N / 8; it += NTHR) {
+      const int p = it / (N / 8), n8 = it - p * (N / 8);
+      const float4 f0 = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8);
+      const float4 f1 = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8 + 4);
+      uint4 v;
+      v.x = pack2(f0.x, f0.y);
+      v.y = pack2(f0.z, f0.w);
+      v.z = pack2(f1.x, f1.y);
+      v.w = pack2(f1.z, f1.w);
+      *reinterpret_cast<uint4 *>(sH + swz<N>(p, 8 * n8)) = v;
+    }
+  }
+  __syncthreads();
+
+  const bf16 *C = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
+  const size_t ldc = (size_t)a.G * N;
+  const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512;
+  const float dsk = a.D ? a.D[h] : 0.f;
+  const bf16 *xg = static_cast<const bf16 *>(a.x);
+  bf16 *yg = static_cast<bf16 *>(a.y);
+
+#pragma unroll 1
+  for (int ti = 0; ti < 2; ++ti) {
+    const int i = ti == 0 ? wave : T - 1 - wave;
+    f32x4 Y[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // (a) state entering the chunk: C h_prev^T, then 2^(cs_l) per row.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 ac[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int row = 32 * i + 16 * u + lr;
+        ac[u] = row < k.len ? ldg8(C + row * ldc + 32 * ks + 8 * lg) : zero8();
+      }
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(sH + swz<N>(16 * pt + lr, 32 * ks + 8 * lg));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(ac[u], bh, Y[u][pt]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = exp2_fast(sCs[32 * i + 16 * u + 4 * lg + r]);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) Y[u][pt][r] *= f;
+      }
+
+    // (b) intra-chunk tiles j <= i.
+    const float cs_r0 = sCs[32 * i];
+    float cs_row[2], rdec[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      cs_row[u] = sCs[32 * i + 16 * u + lr];
+      rdec[u] = exp2_fast(cs_row[u] - cs_r0);
+    }
+#pragma unroll 1
+    for (int j = 0; j <= i; ++j) {
+      const int pair = i * (i + 1) / 2 + j;
+      bf16x8 m[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) m[u] = ldg8(cbase + (size_t)(pair * 2 + u) * 512 + lane * 8);
+      if (j < i) {
+        float q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          q[e] = exp2_fast(cs_r0 - sCs[32 * j + 16 * (e >> 2) + 4 * lg + (e & 3)]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m[u][e] = (bf16)((float)m[u][e] * (rdec[u] * q[e]));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int l = 32 * i + 16 * u + lr;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int s = 32 * j + 16 * (e >> 2) + 4 * lg + (e & 3);
+            const float v = (float)m[u][e] * exp2_fast(cs_row[u] - sCs[s]);
+            m[u][e] = (bf16)(s <= l ? v : 0.f);
+          }
+        }
+      }
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int p = 16 * pt + lr;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(sX + swz<Q>(p, 32 * j + 4 * lg));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(sX + swz<Q>(p, 32 * j + 16 + 4 * lg));
+        bf16x8 xv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[e] = lo[e];
+          xv[4 + e] = hi[e];
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(m[u], xv, Y[u][pt]);
+      }
+    }
+
+    // (c) skip term, round to bf16, store. Lane holds column p, 4 rows.
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int l = 32 * i + 16 * u + 4 * lg + r;
+        if (l < k.len) {
+          const size_t off = ((size_t)(k.start + l) * a.H + h) * kP;
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            const int p = 16 * pt + lr;
+            yg[off + p] = (bf16)(Y[u][pt][r] + dsk * (float)xg[off + p]);
+          }
+        }
+      }
+  }
+}
+
+// ---- launchers ----------------------------------------------------------------
+bool mfma_path_supports(const Args &a) {
+  return a.P == kP && (a.N == 64 || a.N == 128 || a.N == 256) &&
+         (a.Q == 64 || a.Q == 128 || a.Q == 256);
+}
+
+size_t cb_bytes(const Args &a) {
+  const int T = a.Q / 32;
+  return (size_t)a.nc_max * a.G * (T * (T + 1) / 2) * 2 * 1024;
+}
+
+template <int N, int Q>
+static hipError_t launch_nq(const Args &a, bf16 *cb, hipStream_t st, int which) {
+  if (which == 0) {
+    hipLaunchKernelGGL((k_chunk_state_mfma<N, Q>), dim3(a.nc_max, a.H), dim3(256), 0, st, a);
+  } else if (which == 1) {
+    hipLaunchKernelGGL((k_chunk_cb<N, Q>), dim3(a.nc_max, a.G, Q / 64), dim3(64), 0, st, a, cb);
+  } else {
+    hipLaunchKernelGGL((k_chunk_scan_mfma<N, Q>), dim3(a.nc_max, a.H), dim3(Q), 0, st, a,
+                       (const bf16 *)cb);
+  }
+  return hipGetLastError();
+}
+
+template <int N>
+static hipError_t launch_n(const Args &a, bf16 *cb, hipStream_t st, int which) {
+  switch (a.Q) {
+    case 64: return launch_nq<N, 64>(a, cb, st, which);
+    case 128: return launch_nq<N, 128>(a, cb, st, which);
+    default: return launch_nq<N, 256>(a, cb, st, which);
+  }
+}
+
+static hipError_t launch_mfma(const Args &a, void *cb, hipStream_t st, int which) {
+  bf16 *p = static_cast<bf16 *>(cb);
+  switch (a.N) {
+    case 64: return launch_n<64>(a, p, st, which);
+    case 128: return launch_n<128>(a, p, st, which);
+    default: return launch_n<256>(a, p, st, which);
+  }
+}
+
+hipError_t launch_chunk_state_mfma(const Args &a, hipStream_t st) {
+  return launch_mfma(a, nullptr, st, 0);
+}
+hipError_t launch_chunk_cb(const Args &a, void *cb, hipStream_t st) {
+  return launch_mfma(a, cb, st, 1);
+}
+hipError_t launch_chunk_scan_mfma(const Args &a, const void *cb, hipStream_t st) {
+  return launch_mfma(a, const_cast<void *>(cb), st, 2);
+}
+
+}  // namespace ssd

@@ -1,0 +1,70 @@
+// k_plan.hip -- chunk table of a packed varlen batch, built on the device.
+//
+// Packed sequences are independent (the state restarts at every sequence
+// start: tj-hxxt.cn long read of the Mamba-1 paper, part III item 2.3,
+// "Boundary Resetting"). Each sequence is cut into ceil(len/Q) chunks of its
+// own, so no chunk straddles a boundary and the state passing between chunks
+// never crosses sequences. One workgroup scans the per-sequence chunk counts
+// and writes one (sequence, first token, length, index) record per chunk.
+// Malformed cu_seqlens (cu[0] != 0, decreasing, cu[S] != total) set the error
+// word and leave zero chunks, so every later kernel does nothing.
+#include "ssd_internal.h"
+
+namespace ssd {
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
+  __shared__ int s_wave_tot[kPlanThreads / 64];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.nseq, Q = a.Q;
+  int *first = a.plan + 2;  // first chunk of each sequence, then the total
+  int4 *rec = reinterpret_cast<int4 *>(a.plan + a.rec_off);
+  if (tid == 0) s_bad = (a.cu[0] != 0 || a.cu[S] != a.L) ? 1 : 0;
+  __syncthreads();
+
+  int carry = 0;  // chunks of all earlier tiles
+  for (int base = 0; base < S; base += kPlanThreads) {
+    const int s = base + tid;
+    int cnt = 0;
+    if (s < S) {
+      const int lo = a.cu[s], hi = a.cu[s + 1];
+      if (hi < lo || lo < 0 || hi > a.L) s_bad = 1;  // benign race: all write 1
+      else cnt = (hi - lo + Q - 1) / Q;
+    }
+    // Block-wide exclusive scan of cnt: wave scan, then scan of wave totals.
+    const int incl = wave_inclusive_sum(cnt);
+    if (lane == 63) s_wave_tot[wave] = incl;
+    __syncthreads();
+    int before = 0, tile_tot = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      const int t = s_wave_tot[w];
+      before += (w < wave) ? t : 0;
+      tile_tot += t;
+    }
+    if (s < S) first[s] = carry + before + incl - cnt;
+    carry += tile_tot;
+    __syncthreads();
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0 || carry > a.nc_max;
+  if (tid == 0) {
+    a.plan[0] = bad ? 0 : carry;
+    a.plan[1] = bad ? 1 : 0;
+    first[S] = bad ? 0 : carry;
+  }
+  if (bad) return;
+  for (int s = tid; s < S; s += kPlanThreads) {
+    const int lo = a.cu[s], len = a.cu[s + 1] - lo, c0 = first[s];
+    for (int i = 0, off = 0; off < len; ++i, off += Q)
+      rec[c0 + i] = make_int4(s, lo + off, min(Q, len - off), i);
+  }
+}
+
+hipError_t launch_plan(const Args &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

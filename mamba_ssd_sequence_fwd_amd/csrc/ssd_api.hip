@@ -1,0 +1,259 @@
+// ssd_api.hip -- the C ABI (include/ssd.h): validation, workspace layout and
+// the launch sequence of one SSD forward pass.
+//
+// Launch order on the caller's stream (one pass over the hot path):
+//   [varlen] k_plan            chunk table from cu_seqlens (device side)
+//   k_chunk_cumsum             log2-decay prefix inside each chunk
+//   k_chunk_state_{mfma,generic}  per-chunk states from a zero start
+//   k_state_passing            serial recurrence across chunks (in place)
+//   [bf16] k_chunk_cb          C B^T once per (chunk, group)
+//   k_chunk_scan_{mfma,generic}   outputs
+// Nothing is allocated, synchronised or read back; host work is O(1).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ssd.h"
+#include "ssd_internal.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+ssd_status fail(ssd_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  int64_t nc_max;
+  int64_t rec_off;  // int32 offset of the chunk records in the plan area
+  size_t plan, cs, states, cb, total;
+  bool mfma;
+};
+
+bool uses_mfma(const ssd_problem &p) {
+  if (p.dtype != SSD_DTYPE_BF16 || (p.flags & SSD_FLAG_GENERIC_KERNELS)) return false;
+  ssd::Args a{};
+  a.P = p.headdim;
+  a.N = p.dstate;
+  a.Q = p.chunk_size;
+  return ssd::mfma_path_supports(a);
+}
+
+Layout make_layout(const ssd_problem &p) {
+  Layout L{};
+  const int64_t Q = p.chunk_size;
+  L.nc_max = p.num_seqs > 0 ? p.seqlen / Q + p.num_seqs
+                            : (int64_t)p.batch * ((p.seqlen + Q - 1) / Q);
+  L.rec_off = p.num_seqs > 0 ? (int64_t)round_up(3 + (size_t)p.num_seqs, 4) : 0;
+  const size_t plan_ints = p.num_seqs > 0 ? (size_t)(L.rec_off + 4 * L.nc_max) : 4;
+  L.mfma = uses_mfma(p);
+  size_t off = 0;
+  L.plan = off;
+  off = round_up(off + plan_ints * sizeof(int32_t), kAlign);
+  L.cs = off;
+  off = round_up(off + (size_t)L.nc_max * p.nheads * Q * sizeof(float), kAlign);
+  L.states = off;
+  off = round_up(off + (size_t)L.nc_max * p.nheads * p.headdim * p.dstate * sizeof(float), kAlign);
+  L.cb = off;
+  if (L.mfma) {
+    const int64_t T = Q / 32;
+    off = round_up(off + (size_t)L.nc_max * p.ngroups * (T * (T + 1) / 2) * 2 * 1024, kAlign);
+  }
+  L.total = off;
+  return L;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported problem";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *ssd_last_error_detail(void) { return g_detail.c_str(); }
+
+ssd_status ssd_validate(const ssd_problem *p) {
+  g_detail.clear();
+  if (!p) return fail(SSD_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 1 || p->seqlen < 0 || p->nheads < 1 || p->headdim < 1 ||
+      p->dstate < 1 || p->ngroups < 1 || p->chunk_size < 1 || p->num_seqs < 0)
+    return fail(SSD_ERR_INVALID_ARG,
+                "sizes must be positive (batch %d seqlen %d nheads %d headdim %d "
+                "dstate %d ngroups %d chunk_size %d num_seqs %d)",
+                p->batch, p->seqlen, p->nheads, p->headdim, p->dstate, p->ngroups,
+                p->chunk_size, p->num_seqs);
+  if (p->nheads % p->ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "nheads %d not divisible by ngroups %d",
+                p->nheads, p->ngroups);
+  if (p->num_seqs > 0 && p->batch != 1)
+    return fail(SSD_ERR_INVALID_ARG, "varlen (num_seqs %d) needs batch == 1, got %d",
+                p->num_seqs, p->batch);
+  if (p->flags & ~SSD_FLAG_GENERIC_KERNELS)
+    return fail(SSD_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
+  if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+  if (p->headdim != 16 && p->headdim != 32 && p->headdim != 64 && p->headdim != 128)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim %d not in {16, 32, 64, 128}", p->headdim);
+  if (p->dstate % 16 != 0 || p->dstate > 256)
+    return fail(SSD_ERR_UNSUPPORTED, "dstate %d not a multiple of 16 in [16, 256]", p->dstate);
+  if (p->chunk_size != 64 && p->chunk_size != 128 && p->chunk_size != 256)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk_size %d not in {64, 128, 256}", p->chunk_size);
+  if (p->nheads > 65535)
+    return fail(SSD_ERR_UNSUPPORTED, "nheads %d above 65535", p->nheads);
+  const int64_t tokens = (int64_t)p->batch * p->seqlen;
+  if (tokens > INT32_MAX / 2)
+    return fail(SSD_ERR_UNSUPPORTED, "%lld tokens exceed the int32 token index",
+                (long long)tokens);
+  const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->batch;
+  const int64_t sp_blocks = (int64_t)((p->headdim * p->dstate / 4 + 255) / 256) * p->nheads * nseq;
+  const Layout L = make_layout(*p);
+  if (sp_blocks > INT32_MAX || L.nc_max * 4 + L.rec_off > INT32_MAX ||
+      L.nc_max * p->nheads > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "problem too large for 32-bit grid indexing");
+  return SSD_OK;
+}
+
+ssd_status ssd_validate_cu_seqlens(const ssd_problem *p, const int32_t *cu) {
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  if (p->num_seqs <= 0) return fail(SSD_ERR_INVALID_ARG, "problem is not varlen (num_seqs 0)");
+  if (!cu) return fail(SSD_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (cu[0] != 0) return fail(SSD_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  for (int s = 0; s < p->num_seqs; ++s)
+    if (cu[s + 1] < cu[s])
+      return fail(SSD_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s],
+                  cu[s + 1]);
+  if (cu[p->num_seqs] != p->seqlen)
+    return fail(SSD_ERR_INVALID_ARG, "cu_seqlens[%d] = %d, must equal seqlen %d",
+                p->num_seqs, cu[p->num_seqs], p->seqlen);
+  return SSD_OK;
+}
+
+ssd_status ssd_workspace_size(const ssd_problem *p, size_t *bytes) {
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  if (!bytes) return fail(SSD_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_layout(*p).total;
+  return SSD_OK;
+}
+
+ssd_status ssd_get_workspace_layout(const ssd_problem *p, ssd_workspace_layout *out) {
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  if (!out) return fail(SSD_ERR_INVALID_ARG, "layout is NULL");
+  const Layout L = make_layout(*p);
+  out->chunk_cumsum = L.cs;
+  out->chunk_states = L.states;
+  out->chunk_table = L.plan;
+  out->chunk_records = L.rec_off;
+  out->max_chunks = L.nc_max;
+  return SSD_OK;
+}
+
+ssd_status ssd_forward(const ssd_problem *p, const void *x, const void *dt,
+                       const float *A, const void *B, const void *C, const float *D,
+                       const float *initial_state, const int32_t *cu_seqlens, void *y,
+                       float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  const bool varlen = p->num_seqs > 0;
+  const int64_t tokens = (int64_t)p->batch * p->seqlen;
+  if (tokens > 0 && (!x || !dt || !B || !C || !y))
+    return fail(SSD_ERR_INVALID_ARG, "x, dt, B, C and y must be non-NULL");
+  if (!A) return fail(SSD_ERR_INVALID_ARG, "A must be non-NULL");
+  if (varlen && !cu_seqlens) return fail(SSD_ERR_INVALID_ARG, "varlen needs cu_seqlens");
+  if (!varlen && cu_seqlens)
+    return fail(SSD_ERR_INVALID_ARG, "cu_seqlens given but num_seqs is 0");
+  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+      !aligned16(initial_state) || !aligned16(final_state))
+    return fail(SSD_ERR_INVALID_ARG, "x, B, C, y and the states must be 16-byte aligned");
+  const Layout L = make_layout(*p);
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                L.total);
+
+  char *ws = static_cast<char *>(workspace);
+  ssd::Args a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.h0 = initial_state;
+  a.y = y;
+  a.hT = final_state;
+  a.cu = cu_seqlens;
+  a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  a.cs = reinterpret_cast<float *>(ws + L.cs);
+  a.states = reinterpret_cast<float *>(ws + L.states);
+  a.batch = p->batch;
+  a.L = p->seqlen;
+  a.H = p->nheads;
+  a.P = p->headdim;
+  a.N = p->dstate;
+  a.G = p->ngroups;
+  a.Q = p->chunk_size;
+  a.nseq = varlen ? p->num_seqs : p->batch;
+  a.varlen = varlen ? 1 : 0;
+  a.nc_per = varlen ? 0 : (p->seqlen + p->chunk_size - 1) / p->chunk_size;
+  a.nc_max = (int32_t)L.nc_max;
+  a.heads_per_group = p->nheads / p->ngroups;
+  a.rec_off = (int32_t)L.rec_off;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = p->dtype == SSD_DTYPE_BF16;
+
+#define SSD_LAUNCH(call, name)                                                       \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(SSD_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(e_)); \
+  } while (0)
+
+  if (varlen) SSD_LAUNCH(ssd::launch_plan(a, s), "plan");
+  if (a.nc_max > 0) {
+    SSD_LAUNCH(ssd::launch_chunk_cumsum(a, bf, s), "chunk_cumsum");
+    if (L.mfma)
+      SSD_LAUNCH(ssd::launch_chunk_state_mfma(a, s), "chunk_state");
+    else
+      SSD_LAUNCH(ssd::launch_chunk_state_generic(a, bf, s), "chunk_state");
+  }
+  SSD_LAUNCH(ssd::launch_state_passing(a, s), "state_passing");
+  if (a.nc_max > 0) {
+    if (L.mfma) {
+      void *cb = ws + L.cb;
+      SSD_LAUNCH(ssd::launch_chunk_cb(a, cb, s), "chunk_cb");
+      SSD_LAUNCH(ssd::launch_chunk_scan_mfma(a, cb, s), "chunk_scan");
+    } else {
+      SSD_LAUNCH(ssd::launch_chunk_scan_generic(a, bf, s), "chunk_scan");
+    }
+  }
+#undef SSD_LAUNCH
+  return SSD_OK;
+}
+
+}  // extern "C"

@@ -188,3 +188,26 @@ def _np(a):
         import torch
         return a.detach().to("cpu", torch.float64).numpy()
     return np.asarray(a, dtype=np.float64)
+
+
+def chunk_log_decay(dt, A, seq_lens, Q: int):
+    """Natural-log decay from each chunk's start through each of its tokens:
+    sum of dt_k * A_h over the chunk's tokens up to and including token l
+    (the log of the product of the per-step decays exp(dt*A)).
+
+    Returns (chunks, H, Q) fp64 with chunks numbered sequence by sequence and
+    NaN past a partial chunk's end -- the same numbering as the snapshots of
+    :func:`ssd_recurrence`.
+    """
+    dt = np.asarray(_np(dt), np.float64)
+    A = np.asarray(_np(A), np.float64)
+    T, H = dt.shape
+    starts, lens = seq_layout(T, seq_lens)
+    out = []
+    for a, L in zip(starts, lens):
+        for c0 in range(0, int(L), Q):
+            n = min(Q, int(L) - c0)
+            block = np.full((H, Q), np.nan)
+            block[:, :n] = np.cumsum(dt[a + c0:a + c0 + n] * A[None, :], axis=0).T
+            out.append(block)
+    return np.stack(out) if out else np.zeros((0, H, Q))

@@ -1,0 +1,77 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the device,
+run the C-ABI path, run the oracle, compare normwise."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mamba_ssd_sequence_fwd_amd as ssd
+import oracle
+
+# Normwise max relative error bounds: max|gpu - ref| / max|ref| per tensor.
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def to_device(inp: dict, dev="cuda") -> dict:
+    out = {}
+    for k in ("x", "dt", "A", "B", "C", "D", "h0"):
+        out[k] = None if inp[k] is None else inp[k].to(dev)
+    out["cu_seqlens"] = inp["cu_seqlens"]
+    return out
+
+
+def plan_for(inp: dict, chunk=None, generic=False, dev="cuda") -> ssd.Plan:
+    d = to_device(inp, dev)
+    w = inp["workload"]
+    return ssd.Plan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                    chunk_size=chunk or w.chunk, cu_seqlens=d["cu_seqlens"],
+                    generic=generic)
+
+
+def run_gpu(inp: dict, chunk=None, generic=False):
+    """(y (T, H, P) fp64, final_state fp64, plan) after one ssd_forward."""
+    plan = plan_for(inp, chunk, generic)
+    print("[gpu] ssd_forward %s seed=%d %r" % (inp["workload"].name, inp["workload"].seed,
+                                               plan.prob), flush=True)
+    y, hT = plan.run()
+    torch.cuda.synchronize()
+    T = plan.tokens
+    y64 = y.reshape(T, y.shape[2], y.shape[3]).to(torch.float64).cpu().numpy()
+    return y64, hT.to(torch.float64).cpu().numpy(), plan
+
+
+def seq_lens_of(inp: dict):
+    if inp["seq_lens"] is not None:
+        return list(inp["seq_lens"])
+    b, L = inp["x"].shape[:2]
+    return [L] * b
+
+
+def flat_inputs(inp: dict):
+    """(x, dt, B, C) reshaped to the packed-token view the oracle takes."""
+    x = inp["x"]
+    T = x.shape[0] * x.shape[1]
+    return (x.reshape(T, x.shape[2], x.shape[3]), inp["dt"].reshape(T, x.shape[2]),
+            inp["B"].reshape(T, inp["B"].shape[2], inp["B"].shape[3]),
+            inp["C"].reshape(T, inp["C"].shape[2], inp["C"].shape[3]))
+
+
+def run_oracle(inp: dict, snap_every=0):
+    x, dt, B, C = flat_inputs(inp)
+    f = oracle._np
+    return oracle.ssd_recurrence(f(x), f(dt), f(inp["A"]), f(B), f(C), f(inp["D"]),
+                                 None if inp["h0"] is None else f(inp["h0"]),
+                                 seq_lens_of(inp), snap_every=snap_every)
+
+
+def rel_err(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(b)))
+    return float(np.max(np.abs(a - b))) / max(scale, 1e-30)
+
+
+def tol_of(inp: dict) -> float:
+    return TOL[inp["workload"].dtype]

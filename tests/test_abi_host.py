@@ -1,0 +1,137 @@
+"""The C-ABI library on the host: exports, validation, workspace sizing.
+
+No kernel is launched; everything here runs without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_sequence_fwd_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ssd.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.fail("libssd.so not built; run python -m mamba_ssd_sequence_fwd_amd.build")
+    return ssd.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert set(names) == set(ssd.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def P(**kw):
+    base = dict(batch=2, seqlen=1000, nheads=8, headdim=64, dstate=128, ngroups=2,
+                chunk_size=256, num_seqs=0, dtype=ssd.SSD_DTYPE_BF16, flags=0)
+    base.update(kw)
+    return ssd.make_problem(**base)
+
+
+def status_of(fn, *a):
+    try:
+        fn(*a)
+    except ssd.SSDError as e:
+        return e.status
+    return ssd.SSD_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, ssd.SSD_OK),
+    ({"seqlen": 0}, ssd.SSD_OK),
+    ({"batch": 0}, ssd.SSD_ERR_INVALID_ARG),
+    ({"nheads": 0}, ssd.SSD_ERR_INVALID_ARG),
+    ({"ngroups": 3}, ssd.SSD_ERR_INVALID_ARG),
+    ({"num_seqs": 4}, ssd.SSD_ERR_INVALID_ARG),          # batch must be 1
+    ({"batch": 1, "num_seqs": 4}, ssd.SSD_OK),
+    ({"seqlen": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"flags": 8}, ssd.SSD_ERR_INVALID_ARG),
+    ({"dtype": 7}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"headdim": 48}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 24}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 272}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"chunk_size": 100}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"chunk_size": 512}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"seqlen": 2 ** 30}, ssd.SSD_ERR_UNSUPPORTED),
+])
+def test_validate(lib, kw, status):
+    assert status_of(ssd.validate, P(**kw)) == status
+
+
+def test_error_detail_names_the_problem(lib):
+    with pytest.raises(ssd.SSDError) as ei:
+        ssd.validate(P(ngroups=3))
+    assert "ngroups" in str(ei.value)
+
+
+@pytest.mark.parametrize("cu,status", [
+    ([0, 10, 10, 25, 40], ssd.SSD_OK),            # an empty sequence is allowed
+    ([1, 10, 20, 30, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([0, 10, 5, 30, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([0, 10, 20, 30, 39], ssd.SSD_ERR_INVALID_ARG),
+])
+def test_validate_cu_seqlens(lib, cu, status):
+    prob = P(batch=1, seqlen=40, num_seqs=4)
+    assert status_of(ssd.validate_cu_seqlens, prob, cu) == status
+
+
+def test_workspace_layout_dense(lib):
+    prob = P()
+    lay = ssd.workspace_layout(prob)
+    nc = 2 * 4                                   # batch 2, ceil(1000/256) = 4
+    assert lay.max_chunks == nc
+    assert lay.chunk_cumsum % 256 == 0 and lay.chunk_states % 256 == 0
+    assert lay.chunk_states >= lay.chunk_cumsum + nc * 8 * 256 * 4
+    size = ssd.workspace_size(prob)
+    assert size >= lay.chunk_states + nc * 8 * 64 * 128 * 4
+
+
+def test_workspace_layout_varlen_bound(lib):
+    prob = P(batch=1, seqlen=5000, num_seqs=7)
+    lay = ssd.workspace_layout(prob)
+    assert lay.max_chunks == 5000 // 256 + 7
+    assert lay.chunk_records >= 3 + 7 and lay.chunk_records % 4 == 0
+
+
+def test_workspace_grows_with_problem(lib):
+    a = ssd.workspace_size(P(seqlen=1000))
+    b = ssd.workspace_size(P(seqlen=2000))
+    assert b > a
+    # generic kernels need no C.B^T buffer
+    assert ssd.workspace_size(P(flags=ssd.SSD_FLAG_GENERIC_KERNELS)) < a
+
+
+def test_forward_rejects_bad_arguments_before_launch(lib):
+    prob = P()
+    vp = ctypes.c_void_p
+    fake = vp(1 << 20)        # never dereferenced: validation fails first
+    st = lib.ssd_forward(ctypes.byref(prob), fake, fake, fake, fake, fake, None, None,
+                         None, fake, None, None, ctypes.c_size_t(0), None)
+    assert st == ssd.SSD_ERR_WORKSPACE
+    st = lib.ssd_forward(ctypes.byref(prob), None, fake, fake, fake, fake, None, None,
+                         None, fake, None, vp(1 << 21), ctypes.c_size_t(1 << 40), None)
+    assert st == ssd.SSD_ERR_INVALID_ARG
+    st = lib.ssd_forward(ctypes.byref(prob), vp((1 << 20) + 2), fake, fake, fake, fake,
+                         None, None, None, fake, None, vp(1 << 21), ctypes.c_size_t(1 << 40),
+                         None)
+    assert st == ssd.SSD_ERR_INVALID_ARG      # misaligned x
+    st = lib.ssd_forward(ctypes.byref(prob), fake, fake, fake, fake, fake, None, None,
+                         fake, fake, None, vp(1 << 21), ctypes.c_size_t(1 << 40), None)
+    assert st == ssd.SSD_ERR_INVALID_ARG      # cu_seqlens in dense mode
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.ssd_status_string(st)

@@ -1,0 +1,218 @@
+"""GPU path vs the fp64 oracle, element by element (MI355X only).
+
+Small cases span several chunks and a ragged tail and run the full oracle;
+the five workloads at full size compare sampled (sequence, head) pairs, each
+a complete independent run of the recurrence, in the launch configuration the
+benchmark times (one prepared ``Plan`` per workload).
+Tolerance (normwise, per output tensor): 1e-4 for fp32 inputs, 2e-2 for bf16
+inputs with fp32 accumulation and fp32 states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_inputs as si
+from gpu_helpers import (flat_inputs, plan_for, rel_err, run_gpu, run_oracle,
+                         seq_lens_of, tol_of)
+
+pytestmark = pytest.mark.gpu
+
+C = si.CONFIGS
+S = si.STRESS
+SMALL = {
+    "cfg0-tiny-fp32": C[0],
+    "cfg1-ragged": si.scaled(C[1], batch=2, seqlen=700, nheads=6, seed=2001),
+    "cfg2-ragged-h0": si.scaled(C[2], batch=2, seqlen=600, nheads=4, seed=2002),
+    "cfg3-groups-N256": si.scaled(C[3], batch=1, seqlen=1100, nheads=16, ngroups=4, seed=2003),
+    "cfg4-varlen-edges": si.scaled(C[4], nheads=4, num_seqs=7, h0_std=0.1, seed=2004,
+                                   seq_lens=(1, 255, 256, 257, 0, 600, 31)),
+    "S1-slow-decay": si.scaled(S["S1"], batch=2, seqlen=900, nheads=4, seed=2011),
+    "S2-a-zero": si.scaled(S["S2"], batch=1, seqlen=800, nheads=4, seed=2012),
+    "S3-varlen-slow": si.scaled(S["S3"], nheads=4, num_seqs=5, len_range=(100, 900),
+                                seed=2013),
+    "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
+                              chunk=128, seed=2021),
+    "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
+    "fp32-P64-N128": si.scaled(C[2], batch=1, seqlen=600, nheads=3, dtype="fp32", seed=2023),
+    "fp32-varlen": si.scaled(C[4], nheads=2, headdim=16, dstate=32, chunk=64, dtype="fp32",
+                             num_seqs=4, seq_lens=(70, 0, 129, 5), h0_std=0.1, seed=2024),
+}
+
+
+@pytest.fixture(scope="module")
+def small_inputs():
+    return {k: si.make_inputs(w) for k, w in SMALL.items()}
+
+
+@pytest.fixture(scope="module")
+def small_oracle(small_inputs):
+    return {k: run_oracle(v) for k, v in small_inputs.items()}
+
+
+def _compare(inp, got, ref, tol=None):
+    tol = tol or tol_of(inp)
+    (y, hT), (yr, hr) = got, ref
+    assert np.isfinite(y).all() and np.isfinite(hT).all()
+    ey, eh = rel_err(y, yr), rel_err(hT, hr)
+    print("  y err %.3e  final err %.3e  (tol %.0e)" % (ey, eh, tol), flush=True)
+    assert ey <= tol, ("y", ey)
+    assert eh <= tol, ("final_state", eh)
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_parity(case, small_inputs, small_oracle):
+    inp = small_inputs[case]
+    y, hT, _ = run_gpu(inp)
+    _compare(inp, (y, hT), small_oracle[case])
+
+
+@pytest.mark.parametrize("case", [k for k, w in SMALL.items() if w.dtype == "bf16"])
+def test_small_parity_generic_kernels(case, small_inputs, small_oracle):
+    """The plain-FMA kernels on bf16 inputs (the MFMA path's fallback)."""
+    inp = small_inputs[case]
+    y, hT, _ = run_gpu(inp, generic=True)
+    _compare(inp, (y, hT), small_oracle[case])
+
+
+@pytest.mark.parametrize("Q", [64, 128, 256])
+@pytest.mark.parametrize("case", ["cfg2-ragged-h0", "S1-slow-decay", "fp32-P64-N128"])
+def test_chunk_size_invariance(case, Q, small_inputs, small_oracle):
+    inp = small_inputs[case]
+    y, hT, _ = run_gpu(inp, chunk=Q)
+    _compare(inp, (y, hT), small_oracle[case])
+
+
+@pytest.mark.parametrize("case", ["S1-slow-decay", "cfg4-varlen-edges", "S3-varlen-slow",
+                                  "fp32-varlen"])
+def test_intermediates(case, small_inputs):
+    """Chunk log-decay prefix and the state entering every chunk."""
+    inp = small_inputs[case]
+    Q = inp["workload"].chunk
+    y, hT, plan = run_gpu(inp)
+    lay = plan.layout()
+    _, _, snaps = run_oracle(inp, snap_every=Q)
+    nc = snaps.shape[0]
+    H = inp["x"].shape[2]
+    ws = plan.workspace
+    cs = ws[lay.chunk_cumsum:lay.chunk_cumsum + nc * H * Q * 4].view(torch.float32)
+    cs = cs.reshape(nc, H, Q).double().cpu().numpy() * np.log(2.0)
+    x, dt, B, Cm = flat_inputs(inp)
+    ref_cs = oracle.chunk_log_decay(dt, inp["A"], seq_lens_of(inp), Q)
+    mask = np.isfinite(ref_cs)
+    assert rel_err(cs[mask], ref_cs[mask]) < 1e-5
+    P, N = inp["x"].shape[3], inp["B"].shape[3]
+    st = ws[lay.chunk_states:lay.chunk_states + nc * H * P * N * 4].view(torch.float32)
+    st = st.reshape(nc, H, P, N).double().cpu().numpy()
+    assert rel_err(st, snaps) <= tol_of(inp), rel_err(st, snaps)
+
+
+def _run_case(w):
+    inp = si.make_inputs(w)
+    return inp, run_gpu(inp), run_oracle(inp)
+
+
+@pytest.mark.parametrize("w", [
+    si.scaled(C[2], batch=1, seqlen=1, nheads=2, seed=2101),
+    si.scaled(C[2], batch=3, seqlen=37, nheads=2, seed=2102),
+    si.scaled(C[2], batch=1, seqlen=256, nheads=2, seed=2103),
+    si.scaled(C[2], batch=1, seqlen=257, nheads=2, seed=2104),
+    si.scaled(C[1], batch=1, seqlen=512, nheads=3, chunk=64, seed=2105),
+    si.scaled(C[0], seqlen=1, seed=2106),
+    si.scaled(C[4], nheads=2, num_seqs=3, seq_lens=(0, 0, 0), h0_std=0.1, seed=2107),
+    si.scaled(C[4], nheads=2, num_seqs=1, seq_lens=(1,), seed=2108),
+], ids=["L1", "L37-b3", "L256", "L257", "Q64-L512", "fp32-L1", "varlen-all-empty",
+        "varlen-one-token"])
+def test_edge_shapes(w):
+    inp, (y, hT, _), ref = _run_case(w)
+    _compare(inp, (y, hT), ref)
+
+
+def test_empty_dense_batch_returns_initial_state():
+    w = si.scaled(C[2], batch=2, seqlen=0, nheads=2, seed=2109)
+    inp = si.make_inputs(w)
+    y, hT, _ = run_gpu(inp)
+    assert y.size == 0
+    assert np.array_equal(hT, inp["h0"].double().numpy())
+
+
+def test_deterministic(small_inputs):
+    inp = small_inputs["cfg2-ragged-h0"]
+    plan = plan_for(inp)
+    y1, h1 = [t.clone() for t in plan.run()]
+    y2, h2 = plan.run()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_varlen_no_leakage(small_inputs):
+    """Changing one packed sequence changes nothing in the others."""
+    inp = dict(small_inputs["cfg4-varlen-edges"])
+    cu = inp["cu_seqlens"].tolist()
+    y0, h0, _ = run_gpu(inp)
+    k = 3
+    x = inp["x"].clone()
+    x[:, cu[k]:cu[k + 1]] = x[:, cu[k]:cu[k + 1]] * 3 + 1
+    inp["x"] = x
+    y1, h1, _ = run_gpu(inp)
+    for s in range(len(cu) - 1):
+        same = np.array_equal(y0[cu[s]:cu[s + 1]], y1[cu[s]:cu[s + 1]]) and \
+            np.array_equal(h0[s], h1[s])
+        assert same == (s != k or cu[s] == cu[s + 1]), s
+
+
+def test_split_call_continuity(small_inputs):
+    """[0, t) then [t, L) with final -> initial matches one call."""
+    inp = small_inputs["S1-slow-decay"]
+    y, hT, _ = run_gpu(inp)
+    t = 333
+    first = dict(inp)
+    second = dict(inp)
+    for key in ("x", "dt", "B", "C"):
+        first[key] = inp[key][:, :t].contiguous()
+        second[key] = inp[key][:, t:].contiguous()
+    ya, ha, _ = run_gpu(first)
+    second["h0"] = torch.from_numpy(ha).float()
+    yb, hb, _ = run_gpu(second)
+    b, L = inp["x"].shape[:2]
+    ya = ya.reshape(b, t, *ya.shape[1:])
+    yb = yb.reshape(b, L - t, *yb.shape[1:])
+    yy = np.concatenate([ya, yb], axis=1).reshape(y.shape)
+    assert rel_err(yy, y) < 2e-2 and rel_err(hb, hT) < 2e-2
+
+
+# ---- the five workloads at full size ------------------------------------------
+def _sample_pairs(nseq, H, rng, k=10):
+    pairs = {(0, 0), (nseq - 1, H - 1)}
+    while len(pairs) < min(k, nseq * H):
+        pairs.add((int(rng.integers(nseq)), int(rng.integers(H))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_full_workload_sampled(cfg):
+    w = C[cfg]
+    inp = si.make_inputs(w)
+    plan = plan_for(inp)
+    print("[gpu] full workload %d %s %r" % (cfg, w.name, plan.prob), flush=True)
+    y, hT = plan.run()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(hT).all())
+    lens = seq_lens_of(inp)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    H = inp["x"].shape[2]
+    pairs = _sample_pairs(len(lens), H, np.random.default_rng(cfg))
+    x, dt, B, Cm = flat_inputs(inp)
+    ref = oracle.ssd_pairs(x, dt, inp["A"], B, Cm, inp["D"], inp["h0"], lens, pairs)
+    T = plan.tokens
+    yf = y.reshape(T, H, -1)
+    got_y, ref_y, got_h, ref_h = [], [], [], []
+    for (s, h), (yr, hr) in ref.items():
+        got_y.append(yf[starts[s]:starts[s + 1], h].double().cpu().numpy())
+        ref_y.append(yr)
+        got_h.append(hT[s, h].double().cpu().numpy())
+        ref_h.append(hr)
+    ey = rel_err(np.concatenate(got_y), np.concatenate(ref_y))
+    eh = rel_err(np.stack(got_h), np.stack(ref_h))
+    print("  sampled pairs %d: y err %.3e final err %.3e" % (len(pairs), ey, eh), flush=True)
+    assert ey <= tol_of(inp) and eh <= tol_of(inp)
