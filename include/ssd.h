@@ -143,6 +143,28 @@ ssd_status ssd_forward(const ssd_problem *prob, const void *x, const void *dt,
                        const int32_t *cu_seqlens, void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Per-kernel timing of the same launch sequence (a measurement aid).
+ * Runs `iterations` back-to-back forward passes exactly as ssd_forward would
+ * enqueue them, with a HIP event recorded before the first kernel and after
+ * every kernel, then SYNCHRONISES the stream and reports, per kernel, the
+ * summed event-to-event time (kernel duration plus launch gap) in `ms`, and
+ * the first-to-last event time in `total_ms`. Same arguments, outputs and
+ * errors as ssd_forward; creates and destroys its own events. */
+#define SSD_MAX_STAGES 8
+typedef struct ssd_stage_times {
+  int32_t num_stages;
+  int32_t iterations;
+  char names[SSD_MAX_STAGES][24];
+  float ms[SSD_MAX_STAGES];
+  float total_ms;
+} ssd_stage_times;
+ssd_status ssd_forward_timed(const ssd_problem *prob, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C,
+                             const float *D, const float *initial_state,
+                             const int32_t *cu_seqlens, void *y, float *final_state,
+                             void *workspace, size_t workspace_bytes, void *stream,
+                             int32_t iterations, ssd_stage_times *times);
+
 /* Where ssd_forward leaves its intermediates inside the workspace (byte
  * offsets), for inspection after the stream has completed:
  *   chunk_cumsum  fp32 (chunks, H, Q): inclusive prefix of dt*A*log2(e)

@@ -44,9 +44,25 @@ class WorkspaceLayout(ctypes.Structure):
                 ("max_chunks", ctypes.c_int64)]
 
 
+MAX_STAGES = 8
+
+
+class StageTimes(ctypes.Structure):
+    _fields_ = [("num_stages", ctypes.c_int32), ("iterations", ctypes.c_int32),
+                ("names", (ctypes.c_char * 24) * MAX_STAGES),
+                ("ms", ctypes.c_float * MAX_STAGES), ("total_ms", ctypes.c_float)]
+
+    def as_dict(self):
+        """{kernel name: mean ms per launch}, plus '_total_ms' (all iterations)."""
+        out = {self.names[k].value.decode(): self.ms[k] / max(self.iterations, 1)
+               for k in range(self.num_stages)}
+        out["_total_ms"] = self.total_ms
+        return out
+
+
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-            "ssd_forward", "ssd_get_workspace_layout", "ssd_status_string",
-            "ssd_last_error_detail")
+            "ssd_forward", "ssd_forward_timed", "ssd_get_workspace_layout",
+            "ssd_status_string", "ssd_last_error_detail")
 
 _lock = threading.Lock()
 _lib = None
@@ -70,8 +86,10 @@ def load(path: str = LIB_PATH):
         lib.ssd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssd_get_workspace_layout.argtypes = [P, ctypes.POINTER(WorkspaceLayout)]
         lib.ssd_forward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
+        lib.ssd_forward_timed.argtypes = ([P] + [vp] * 11 + [ctypes.c_size_t, vp, ctypes.c_int32,
+                                          ctypes.POINTER(StageTimes)])
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-                  "ssd_get_workspace_layout", "ssd_forward"):
+                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -199,6 +217,21 @@ class Plan:
             _ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()),
             ctypes.c_void_p(stream.cuda_stream)), "ssd_forward")
         return self.y, self.final_state
+
+    def run_timed(self, iterations: int, stream=None) -> StageTimes:
+        """``iterations`` passes with a HIP event after every kernel; waits for
+        them and returns the per-kernel times (see ssd_forward_timed)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.y.device)
+        x, dt, A, B, C, D, h0 = self.inputs
+        times = StageTimes()
+        _check(load().ssd_forward_timed(
+            ctypes.byref(self.prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(h0), _ptr(self.cu), _ptr(self.y), _ptr(self.final_state),
+            _ptr(self.workspace), ctypes.c_size_t(self.workspace.numel()),
+            ctypes.c_void_p(stream.cuda_stream), int(iterations), ctypes.byref(times)),
+            "ssd_forward_timed")
+        return times
 
     def layout(self) -> WorkspaceLayout:
         return workspace_layout(self.prob)

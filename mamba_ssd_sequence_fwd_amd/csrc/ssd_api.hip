@@ -12,7 +12,10 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <string.h>
+
 #include <string>
+#include <vector>
 
 #include "ssd.h"
 #include "ssd_internal.h"
@@ -75,6 +78,126 @@ Layout make_layout(const ssd_problem &p) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+ssd_status check_args(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                      const void *B, const void *C, const int32_t *cu_seqlens, const void *y,
+                      const float *initial_state, const float *final_state,
+                      const void *workspace, size_t workspace_bytes) {
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  const bool varlen = p->num_seqs > 0;
+  const int64_t tokens = (int64_t)p->batch * p->seqlen;
+  if (tokens > 0 && (!x || !dt || !B || !C || !y))
+    return fail(SSD_ERR_INVALID_ARG, "x, dt, B, C and y must be non-NULL");
+  if (!A) return fail(SSD_ERR_INVALID_ARG, "A must be non-NULL");
+  if (varlen && !cu_seqlens) return fail(SSD_ERR_INVALID_ARG, "varlen needs cu_seqlens");
+  if (!varlen && cu_seqlens)
+    return fail(SSD_ERR_INVALID_ARG, "cu_seqlens given but num_seqs is 0");
+  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+      !aligned16(initial_state) || !aligned16(final_state))
+    return fail(SSD_ERR_INVALID_ARG, "x, B, C, y and the states must be 16-byte aligned");
+  const Layout L = make_layout(*p);
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                L.total);
+  return SSD_OK;
+}
+
+ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const void *dt,
+                    const float *A, const void *B, const void *C, const float *D,
+                    const float *initial_state, const int32_t *cu_seqlens, void *y,
+                    float *final_state, void *workspace) {
+  const bool varlen = p->num_seqs > 0;
+  char *ws = static_cast<char *>(workspace);
+  ssd::Args a{};
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.h0 = initial_state;
+  a.y = y;
+  a.hT = final_state;
+  a.cu = cu_seqlens;
+  a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
+  a.cs = reinterpret_cast<float *>(ws + L.cs);
+  a.states = reinterpret_cast<float *>(ws + L.states);
+  a.cb = ws + L.cb;
+  a.batch = p->batch;
+  a.L = p->seqlen;
+  a.H = p->nheads;
+  a.P = p->headdim;
+  a.N = p->dstate;
+  a.G = p->ngroups;
+  a.Q = p->chunk_size;
+  a.nseq = varlen ? p->num_seqs : p->batch;
+  a.varlen = varlen ? 1 : 0;
+  a.nc_per = varlen ? 0 : (p->seqlen + p->chunk_size - 1) / p->chunk_size;
+  a.nc_max = (int32_t)L.nc_max;
+  a.heads_per_group = p->nheads / p->ngroups;
+  a.rec_off = (int32_t)L.rec_off;
+  return a;
+}
+
+struct StageNames {
+  int count;
+  const char *name[SSD_MAX_STAGES];
+};
+
+StageNames stage_names(const ssd::Args &a, const Layout &L, bool) {
+  StageNames n{};
+  if (a.varlen) n.name[n.count++] = "plan";
+  if (a.nc_max > 0) {
+    n.name[n.count++] = "chunk_cumsum";
+    n.name[n.count++] = "chunk_state";
+  }
+  n.name[n.count++] = "state_passing";
+  if (a.nc_max > 0) {
+    if (L.mfma) n.name[n.count++] = "chunk_cb";
+    n.name[n.count++] = "chunk_scan";
+  }
+  return n;
+}
+
+// Enqueue the whole pass; with `ev` non-null, record ev[0] before the first
+// kernel and ev[k+1] after stage k (for per-kernel timing).
+ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
+                   hipEvent_t *ev) {
+  int k = 0;
+  auto mark = [&]() -> bool {
+    return ev == nullptr || hipEventRecord(ev[k++], s) == hipSuccess;
+  };
+#define SSD_LAUNCH(call, name)                                                       \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(SSD_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(e_)); \
+    if (!mark()) return fail(SSD_ERR_HIP, "hipEventRecord failed after %s", name);   \
+  } while (0)
+  if (!mark()) return fail(SSD_ERR_HIP, "hipEventRecord failed");
+  if (a.varlen) SSD_LAUNCH(ssd::launch_plan(a, s), "plan");
+  if (a.nc_max > 0) {
+    SSD_LAUNCH(ssd::launch_chunk_cumsum(a, bf, s), "chunk_cumsum");
+    if (L.mfma)
+      SSD_LAUNCH(ssd::launch_chunk_state_mfma(a, s), "chunk_state");
+    else
+      SSD_LAUNCH(ssd::launch_chunk_state_generic(a, bf, s), "chunk_state");
+  }
+  SSD_LAUNCH(ssd::launch_state_passing(a, s), "state_passing");
+  if (a.nc_max > 0) {
+    if (L.mfma) {
+      SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
+      SSD_LAUNCH(ssd::launch_chunk_scan_mfma(a, a.cb, s), "chunk_scan");
+    } else {
+      SSD_LAUNCH(ssd::launch_chunk_scan_generic(a, bf, s), "chunk_scan");
+    }
+  }
+#undef SSD_LAUNCH
+  return SSD_OK;
+}
 
 }  // namespace
 
@@ -176,84 +299,65 @@ ssd_status ssd_forward(const ssd_problem *p, const void *x, const void *dt,
                        const float *initial_state, const int32_t *cu_seqlens, void *y,
                        float *final_state, void *workspace, size_t workspace_bytes,
                        void *stream) {
-  ssd_status st = ssd_validate(p);
+  ssd_status st = check_args(p, x, dt, A, B, C, cu_seqlens, y, initial_state, final_state,
+                             workspace, workspace_bytes);
   if (st != SSD_OK) return st;
-  const bool varlen = p->num_seqs > 0;
-  const int64_t tokens = (int64_t)p->batch * p->seqlen;
-  if (tokens > 0 && (!x || !dt || !B || !C || !y))
-    return fail(SSD_ERR_INVALID_ARG, "x, dt, B, C and y must be non-NULL");
-  if (!A) return fail(SSD_ERR_INVALID_ARG, "A must be non-NULL");
-  if (varlen && !cu_seqlens) return fail(SSD_ERR_INVALID_ARG, "varlen needs cu_seqlens");
-  if (!varlen && cu_seqlens)
-    return fail(SSD_ERR_INVALID_ARG, "cu_seqlens given but num_seqs is 0");
-  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
-      !aligned16(initial_state) || !aligned16(final_state))
-    return fail(SSD_ERR_INVALID_ARG, "x, B, C, y and the states must be 16-byte aligned");
   const Layout L = make_layout(*p);
-  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
-    return fail(SSD_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
-  if (workspace_bytes < L.total)
-    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                L.total);
+  const ssd::Args a = make_args(p, L, x, dt, A, B, C, D, initial_state, cu_seqlens, y,
+                                final_state, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return enqueue(a, L, p->dtype == SSD_DTYPE_BF16, s, nullptr);
+}
 
-  char *ws = static_cast<char *>(workspace);
-  ssd::Args a{};
-  a.x = x;
-  a.dt = dt;
-  a.A = A;
-  a.B = B;
-  a.C = C;
-  a.D = D;
-  a.h0 = initial_state;
-  a.y = y;
-  a.hT = final_state;
-  a.cu = cu_seqlens;
-  a.plan = reinterpret_cast<int32_t *>(ws + L.plan);
-  a.cs = reinterpret_cast<float *>(ws + L.cs);
-  a.states = reinterpret_cast<float *>(ws + L.states);
-  a.batch = p->batch;
-  a.L = p->seqlen;
-  a.H = p->nheads;
-  a.P = p->headdim;
-  a.N = p->dstate;
-  a.G = p->ngroups;
-  a.Q = p->chunk_size;
-  a.nseq = varlen ? p->num_seqs : p->batch;
-  a.varlen = varlen ? 1 : 0;
-  a.nc_per = varlen ? 0 : (p->seqlen + p->chunk_size - 1) / p->chunk_size;
-  a.nc_max = (int32_t)L.nc_max;
-  a.heads_per_group = p->nheads / p->ngroups;
-  a.rec_off = (int32_t)L.rec_off;
+ssd_status ssd_forward_timed(const ssd_problem *p, const void *x, const void *dt,
+                             const float *A, const void *B, const void *C, const float *D,
+                             const float *initial_state, const int32_t *cu_seqlens,
+                             void *y, float *final_state, void *workspace,
+                             size_t workspace_bytes, void *stream, int32_t iterations,
+                             ssd_stage_times *times) {
+  if (iterations < 1 || !times)
+    return fail(SSD_ERR_INVALID_ARG, "iterations must be >= 1 and times non-NULL");
+  // Validate by a dry run of the argument checks of ssd_forward.
+  ssd_status st = check_args(p, x, dt, A, B, C, cu_seqlens, y, initial_state, final_state,
+                             workspace, workspace_bytes);
+  if (st != SSD_OK) return st;
+  const Layout L = make_layout(*p);
+  ssd::Args a = make_args(p, L, x, dt, A, B, C, D, initial_state, cu_seqlens, y, final_state,
+                          workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = p->dtype == SSD_DTYPE_BF16;
-
-#define SSD_LAUNCH(call, name)                                                       \
-  do {                                                                               \
-    hipError_t e_ = (call);                                                          \
-    if (e_ != hipSuccess)                                                            \
-      return fail(SSD_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(e_)); \
-  } while (0)
-
-  if (varlen) SSD_LAUNCH(ssd::launch_plan(a, s), "plan");
-  if (a.nc_max > 0) {
-    SSD_LAUNCH(ssd::launch_chunk_cumsum(a, bf, s), "chunk_cumsum");
-    if (L.mfma)
-      SSD_LAUNCH(ssd::launch_chunk_state_mfma(a, s), "chunk_state");
-    else
-      SSD_LAUNCH(ssd::launch_chunk_state_generic(a, bf, s), "chunk_state");
-  }
-  SSD_LAUNCH(ssd::launch_state_passing(a, s), "state_passing");
-  if (a.nc_max > 0) {
-    if (L.mfma) {
-      void *cb = ws + L.cb;
-      SSD_LAUNCH(ssd::launch_chunk_cb(a, cb, s), "chunk_cb");
-      SSD_LAUNCH(ssd::launch_chunk_scan_mfma(a, cb, s), "chunk_scan");
-    } else {
-      SSD_LAUNCH(ssd::launch_chunk_scan_generic(a, bf, s), "chunk_scan");
+  StageNames names = stage_names(a, L, bf);
+  const int ns = names.count;
+  std::vector<hipEvent_t> ev((size_t)iterations * (ns + 1));
+  for (auto &e : ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto &f : ev) if (f) (void)hipEventDestroy(f);
+      return fail(SSD_ERR_HIP, "hipEventCreate failed");
     }
+  ssd_status rc = SSD_OK;
+  for (int it = 0; it < iterations && rc == SSD_OK; ++it)
+    rc = enqueue(a, L, bf, s, &ev[(size_t)it * (ns + 1)]);
+  if (rc == SSD_OK && hipStreamSynchronize(s) != hipSuccess)
+    rc = fail(SSD_ERR_HIP, "stream synchronisation failed");
+  if (rc == SSD_OK) {
+    memset(times, 0, sizeof(*times));
+    times->num_stages = ns;
+    for (int k = 0; k < ns; ++k) snprintf(times->names[k], sizeof(times->names[k]), "%s", names.name[k]);
+    for (int it = 0; it < iterations; ++it) {
+      hipEvent_t *e = &ev[(size_t)it * (ns + 1)];
+      for (int k = 0; k < ns; ++k) {
+        float ms = 0.f;
+        (void)hipEventElapsedTime(&ms, e[k], e[k + 1]);
+        times->ms[k] += ms;
+      }
+    }
+    float tot = 0.f;
+    (void)hipEventElapsedTime(&tot, ev[0], ev[ev.size() - 1]);
+    times->total_ms = tot;
+    times->iterations = iterations;
   }
-#undef SSD_LAUNCH
-  return SSD_OK;
+  for (auto &e : ev) (void)hipEventDestroy(e);
+  return rc;
 }
 
 }  // extern "C"

@@ -25,6 +25,7 @@ struct Args {
   int32_t *plan;        // chunk table (varlen)
   float *cs;            // (chunks, H, Q): log2 decay prefix inside the chunk
   float *states;        // (chunks, H, P, N)
+  void *cb;             // bf16 C B^T tiles (MFMA path only)
   int32_t batch, L, H, P, N, G, Q;
   int32_t nseq;         // sequences: batch (dense) or num_seqs (varlen)
   int32_t varlen;       // 0 / 1
