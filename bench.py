@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the SSD forward pass on one MI355X.
+
+One step = one ssd_forward over one batch of synthetic input (every kernel of
+the path). Default workload: the 2.7B-shaped config (batch 8, L 2048, H 80,
+P 64, N 128, G 1, chunk 256, bf16 in / fp32 accumulate and states, random
+fp32 initial state). Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line with: whole-job tokens/s, the per-kernel times measured
+live with HIP events over the timed region, the roofline of the dominant
+kernel (algorithmic bytes or flops per launch / its mean event time), and the
+fp64 CPU oracle timed on this host (a reported baseline, not a target).
+
+    python bench.py [--steps K] [--warmup W] [--config 0..4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ssd_inputs as si  # noqa: E402
+import mamba_ssd_sequence_fwd_amd as ssd  # noqa: E402
+
+METRIC = "SSD fwd tokens/sec + % MFMA/HBM roofline at L=2048, H=80, P=64, N=128"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
+    """Bytes each kernel must move and flops it must do, by the method's
+    definition (unique HBM bytes; causal pairs only; C B^T once per group).
+
+    Per (chunk, head) unit with q tokens: x q*P*e, y q*P*e, dt q*e, state
+    P*N*4 (fp32), cumsum q*4; per (chunk, group): B and C q*N*e each.
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    lens = inp["seq_lens"] or [w.seqlen] * w.batch
+    H, P, N, G, Q = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    T = int(sum(lens))
+    chunks = [min(Q, L - c0) for L in lens for c0 in range(0, L, Q)]
+    nc = len(chunks)
+    S = len(lens)
+    state = P * N * 4
+    causal = sum(q * (q + 1) // 2 for q in chunks)           # (l, s) pairs, s <= l
+    cost = {
+        "chunk_cumsum": dict(bytes=T * H * e + T * H * 4, flops=2 * T * H),
+        "chunk_state": dict(bytes=T * H * P * e + T * H * (e + 4) + T * G * N * e
+                            + nc * H * state, flops=2 * T * H * P * N),
+        "state_passing": dict(bytes=2 * nc * H * state + 2 * S * H * state * (
+            1 if inp["h0"] is not None else 0.5), flops=2 * nc * H * P * N),
+        "chunk_cb": dict(bytes=2 * T * G * N * e + causal * G * 2, flops=2 * causal * G * N),
+        "chunk_scan": dict(bytes=2 * T * H * P * e + T * H * e + T * G * N * e + nc * H * state
+                           + T * H * 4 + causal * G * 2,
+                           flops=2 * causal * H * P + 2 * T * H * N * P),
+    }
+    cost["ssd_fused"] = dict(
+        bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + causal * G * 2 + S * H * state * (
+            2 if inp["h0"] is not None else 1),
+        flops=2 * causal * H * P + 4 * T * H * N * P + 2 * nc * H * P * N)
+    cost["_path"] = dict(
+        bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + S * H * state * (
+            2 if inp["h0"] is not None else 1),
+        flops=2 * causal * (G * N + H * P) + 4 * T * H * N * P)
+    return cost
+
+
+def cpu_baseline(inp: dict, w: si.Workload, budget_s: float) -> dict:
+    """Time the fp64 oracle (as it stands) on this host over a bounded sample
+    of (sequence, head) pairs of the same workload; scale to tokens/s."""
+    import oracle
+    threads = oracle.default_threads()
+    lens = inp["seq_lens"] or [w.seqlen] * w.batch
+    H = w.nheads
+    x = inp["x"].reshape(-1, H, w.headdim)
+    dt = inp["dt"].reshape(-1, H)
+    B = inp["B"].reshape(-1, w.ngroups, w.dstate)
+    C = inp["C"].reshape(-1, w.ngroups, w.dstate)
+    all_pairs = [(s, h) for s in range(len(lens)) for h in range(H)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(all_pairs))
+    # Probe with one pair per thread, then size the sample to the budget.
+    n = min(len(all_pairs), threads)
+    done, tok, elapsed = 0, 0, 0.0
+    while done < len(all_pairs):
+        batch = [all_pairs[i] for i in order[done:done + n]]
+        t0 = time.perf_counter()
+        oracle.ssd_pairs(x, dt, inp["A"], B, C, inp["D"], inp["h0"], lens, batch,
+                         threads=threads)
+        elapsed += time.perf_counter() - t0
+        tok += sum(lens[s] for s, _ in batch)
+        done += len(batch)
+        if elapsed > budget_s:
+            break
+        rate = elapsed / max(done, 1)
+        n = int(min(len(all_pairs) - done, max(threads, (budget_s - elapsed) / max(rate, 1e-9))))
+        if n <= 0:
+            break
+    # tokens of the whole workload per second: each pair is one head of one
+    # sequence; the job has H heads per token.
+    value = tok / H / elapsed
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d (sequence, head) pairs of the %s workload, %.1f s of "
+                      "fp64 recurrence over %d host threads" % (
+                          done, len(all_pairs), w.name, elapsed, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run one kernel per step of the method instead of the fused kernel")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device-to-device copy "
+                         "of this many MiB (known HBM traffic) to calibrate byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the SSD forward pass here runs on a single "
+              "MI355X (no sharding, no collectives); --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": max(args.steps, 1)}), flush=True)
+        return
+
+    w = si.CONFIGS[args.config]
+    inp = si.make_inputs(w)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("x", "dt", "A", "B", "C",
+                                                                   "D", "h0")}
+    plan = ssd.Plan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                    chunk_size=w.chunk, cu_seqlens=inp["cu_seqlens"], unfused=args.unfused)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        plan.run(stream)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, every kernel bracketed by HIP events on the
+    # stream the kernels run on; the call synchronises at the end.
+    t0 = time.perf_counter()
+    times = plan.run_timed(args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel_ms = times.as_dict()
+    total_ms = per_kernel_ms.pop("_total_ms")
+    ms_per_step = total_ms / args.steps
+    tokens = plan.tokens
+    value = tokens / (ms_per_step / 1e3)
+
+    cost = algorithmic_cost(w, inp)
+    kernels = {}
+    for name, ms in per_kernel_ms.items():
+        c = cost.get(name, {"bytes": 0, "flops": 0})
+        kernels[name] = {"ms": round(ms, 5), "alg_bytes": int(c["bytes"]),
+                         "alg_flops": int(c["flops"]),
+                         "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
+                         "TFLOP/s": round(c["flops"] / (ms * 1e-3) / 1e12, 2)}
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    kd = kernels[dom]
+    # Every kernel of this path is HBM-bound by its algorithmic intensity
+    # (flops/byte far below the bf16 ridge of ~312), so the roof is HBM.
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "mfma_frac": round(kd["TFLOP/s"] / (MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16"
+                                                    else MFMA_FP32_PEAK_TFLOPS), 4)}
+    path = cost["_path"]
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32", "data": "synthetic",
+        "config": {"workload": w.name, "kernels": "unfused" if args.unfused else "default", "batch": w.batch if not w.num_seqs else 1,
+                   "seq_len": plan.prob.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk,
+                   "num_seqs": w.num_seqs, "tokens_per_step": tokens,
+                   "initial_state": inp["h0"] is not None},
+        "roofline": roofline,
+        "path": {"alg_bytes": int(path["bytes"]), "alg_flops": int(path["flops"]),
+                 "GB/s": round(path["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(path["bytes"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "TFLOP/s": round(path["flops"] / (ms_per_step * 1e-3) / 1e12, 2)},
+        "kernels": kernels,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,6 +60,12 @@ typedef enum ssd_dtype {
 /* Flags for ssd_problem.flags. */
 #define SSD_FLAG_GENERIC_KERNELS 1u /* use the plain FMA kernels even where the
                                        MFMA kernels apply (testing aid) */
+#define SSD_FLAG_UNFUSED 2u         /* one kernel per step of the method
+                                       (cumsum, chunk state, state passing,
+                                       chunk scan) with per-chunk states in
+                                       the workspace, instead of the fused
+                                       kernel that bf16 problems use by
+                                       default */
 
 /*
  * Problem description.
@@ -167,6 +173,9 @@ ssd_status ssd_forward_timed(const ssd_problem *prob, const void *x, const void 
 
 /* Where ssd_forward leaves its intermediates inside the workspace (byte
  * offsets), for inspection after the stream has completed:
+ * The per-chunk intermediates exist only when the per-step kernels run
+ * (fp32 problems, shapes the fused kernel does not cover, SSD_FLAG_UNFUSED);
+ * the fused kernel keeps them on chip and the workspace has no room for them.
  *   chunk_cumsum  fp32 (chunks, H, Q): inclusive prefix of dt*A*log2(e)
  *                 inside each chunk, i.e. the base-2 logarithm of the decay
  *                 from the chunk's start through each token (entries past a

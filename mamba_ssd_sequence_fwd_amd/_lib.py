@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libssd.so")
 SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP = range(5)
 SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
 SSD_FLAG_GENERIC_KERNELS = 1
+SSD_FLAG_UNFUSED = 2
 
 
 class SSDError(RuntimeError):
@@ -159,7 +160,7 @@ class Plan:
 
     def __init__(self, x, dt, A, B, C, D=None, initial_state=None, chunk_size=256,
                  cu_seqlens=None, *, want_final_state=True, generic=False,
-                 check_cu_seqlens=True):
+                 unfused=False, check_cu_seqlens=True):
         if x.dim() != 4:
             raise ValueError("x must be (batch, seqlen, nheads, headdim)")
         batch, L, H, P = x.shape
@@ -190,7 +191,8 @@ class Plan:
             raise ValueError("initial_state must be (%d, %d, %d, %d) float32" % (nstate, H, P, N))
         self.prob = make_problem(batch, L, H, P, N, G, chunk_size, num_seqs,
                                  _DTYPES[x.dtype],
-                                 SSD_FLAG_GENERIC_KERNELS if generic else 0)
+                                 (SSD_FLAG_GENERIC_KERNELS if generic else 0)
+                                 | (SSD_FLAG_UNFUSED if unfused else 0))
         validate(self.prob)
         if cu_seqlens is not None:
             if check_cu_seqlens or cu_seqlens.device.type == "cpu":

@@ -26,10 +26,19 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(Args a) {
   const int h0 = blockIdx.y * kCsHeads;
   const int nh = min(kCsHeads, a.H - h0);
   const int tid = threadIdx.x;
-  for (int e = tid; e < k.len * nh; e += 256) {
-    const int l = e / nh, j = e - l * nh;
-    const float v = ld<T>(a.dt, (size_t)(k.start + l) * a.H + h0 + j);
-    s_da[j][l] = v * a.A[h0 + j] * kLog2e;
+  {
+    // One token row per thread: its (up to) 16 head values are independent
+    // loads, all issued before the LDS writes.
+    const int l = tid, lc = min(l, k.len - 1);
+    float v[kCsHeads];
+#pragma unroll
+    for (int j = 0; j < kCsHeads; ++j)  // unconditional loads (clamped), then select
+      v[j] = ld<T>(a.dt, (size_t)(k.start + lc) * a.H + h0 + min(j, nh - 1));
+#pragma unroll
+    for (int j = 0; j < kCsHeads; ++j) v[j] = (l < k.len) ? v[j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kCsHeads; ++j)
+      if (j < nh) s_da[j][l] = v[j] * a.A[h0 + j] * kLog2e;
   }
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;

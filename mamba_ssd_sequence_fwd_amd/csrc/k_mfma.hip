@@ -25,66 +25,9 @@
 // LDS tiles are [row][col] bf16 with 16-byte chunks XOR-swizzled by (row & 7)
 // so that the 16 rows an MFMA operand read touches fall in distinct banks.
 #include "ssd_internal.h"
+#include "mfma_common.h"
 
 namespace ssd {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kP = 64;
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 zero8() {
-  bf16x8 z;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.f;
-  return z;
-}
-
-// Element offset of (row, col) in a swizzled [rows][W] bf16 LDS tile.
-template <int W>
-__device__ __forceinline__ int swz(int row, int col) {
-  return row * W + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
-}
-
-__device__ __forceinline__ bf16x8 ldg8(const bf16 *p) {
-  return *reinterpret_cast<const bf16x8 *>(p);
-}
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const bf16 a = (bf16)lo, b = (bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
-// Stage rows [s0, s0 + 2*npairs) of a token-major bf16 matrix (row stride
-// `ld` elements, W columns used, rows >= len read as zero) into a transposed,
-// swizzled LDS tile dst[col][s - s0] (row width WT), scaling token s by
-// scale[s]. Each work item moves 2 tokens x 8 columns with two 16-byte loads
-// and eight 32-bit LDS stores (token pairs packed).
-template <int W, int WT, int NTHR>
-__device__ __forceinline__ void stage_transposed(bf16 *dst, const bf16 *src,
-                                                 size_t ld, int s0, int npairs,
-                                                 int len, const float *scale) {
-  const int items = npairs * (W / 8);
-  for (int it = threadIdx.x; it < items; it += NTHR) {
-    const int sp = it % npairs, cg = it / npairs;
-    const int s = s0 + 2 * sp;
-    bf16x8 v0 = zero8(), v1 = zero8();
-    if (s < len) v0 = ldg8(src + (size_t)s * ld + 8 * cg);
-    if (s + 1 < len) v1 = ldg8(src + (size_t)(s + 1) * ld + 8 * cg);
-    const float w0 = scale[s], w1 = scale[s + 1];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t pr = pack2((float)v0[e] * w0, (float)v1[e] * w1);
-      *reinterpret_cast<uint32_t *>(dst + swz<WT>(8 * cg + e, 2 * sp)) = pr;
-    }
-  }
-}
 
 // ============================================================================
 // chunk_state: S_c[p, n] = sum_s w_s x_s[p] B_s[n]
@@ -98,24 +41,31 @@ __global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
   __shared__ __attribute__((aligned(16))) bf16 sX[kP * QH];
   __shared__ __attribute__((aligned(16))) bf16 sB[N * QH];
   __shared__ float sW[Q];
-  __shared__ float sOne[Q];
   Chunk k;
   const int c = blockIdx.x;
   if (!chunk_of(a, c, k)) return;
   const int h = blockIdx.y, g = h / a.heads_per_group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
-  const float last = cs[k.len - 1];
-  for (int l = tid; l < Q; l += 256) {
-    sW[l] = (l < k.len)
-                ? exp2_fast(last - cs[l]) *
-                      (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + l) * a.H + h]
-                : 0.f;
-    sOne[l] = 1.f;
-  }
   const bf16 *xsrc = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
   const bf16 *bsrc = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
+  Stager<kP, QH / 2, 256> sx;
+  Stager<N, QH / 2, 256> sb;
+  sx.load(xsrc, (size_t)a.H * kP, 0, k.len);
+  sb.load(bsrc, (size_t)a.G * N, 0, k.len);
+
+  const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
+  const float last = cs[k.len - 1];
+#pragma unroll
+  for (int q = 0; q < (Q + 255) / 256; ++q) {
+    const int l = tid + 256 * q;
+    if (Q >= 256 || l < Q) {
+      const int lc = min(l, k.len - 1);
+      const float w = exp2_fast(last - cs[lc]) *
+                      (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h];
+      sW[l] = l < k.len ? w : 0.f;
+    }
+  }
 
   f32x4 acc[4][NT];
 #pragma unroll
@@ -123,11 +73,15 @@ __global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[pt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+#pragma unroll
   for (int s0 = 0; s0 < Q; s0 += QH) {
-    __syncthreads();
-    stage_transposed<kP, QH, 256>(sX, xsrc, (size_t)a.H * kP, s0, QH / 2, k.len, sW);
-    stage_transposed<N, QH, 256>(sB, bsrc, (size_t)a.G * N, s0, QH / 2, k.len,
-                                 sOne);
+    __syncthreads();  // previous half consumed; sW visible
+    sx.template store<QH>(sX, s0, sW);
+    sb.template store<QH>(sB, s0, nullptr);
+    if (s0 + QH < Q) {  // next half's loads overlap this half's MFMAs
+      sx.load(xsrc, (size_t)a.H * kP, s0 + QH, k.len);
+      sb.load(bsrc, (size_t)a.G * N, s0 + QH, k.len);
+    }
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < QH / 32; ++ks) {
@@ -186,7 +140,7 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
       const int row = 32 * i + 16 * u + lr;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        cop[u][ks] = row < k.len ? ldg8(C + row * ldr + 32 * ks + 8 * lg) : zero8();
+        cop[u][ks] = ldg8_row(C, ldr, row, k.len, 32 * ks + 8 * lg);
     }
 #pragma unroll 1
     for (int j = 0; j <= i; ++j) {
@@ -200,7 +154,7 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int srow = 32 * j + 16 * t + lr;
-          const bf16x8 bop = srow < k.len ? ldg8(B + srow * ldr + 32 * ks + 8 * lg) : zero8();
+          const bf16x8 bop = ldg8_row(B, ldr, srow, k.len, 32 * ks + 8 * lg);
 #pragma unroll
           for (int u = 0; u < 2; ++u) acc[u][t] = mfma(bop, cop[u][ks], acc[u][t]);
         }
@@ -223,15 +177,18 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
 // chunk_scan: y_l = 2^(cs_l) C_l h_prev^T + sum_{s<=l} CB[l,s] 2^(cs_l - cs_s)
 //             dt_s x_s + D x_l.
 // One workgroup per (chunk, head) with Q/64 waves; wave w owns the 32-row
-// tiles w and T-1-w (equal work per wave). (dt o x)^T and h_prev (bf16) sit in
-// LDS; C rows and the precomputed CB tiles are read straight into registers.
-// Off-diagonal tiles (j < i) split the decay at the tile's first row r0:
-// 2^(cs_l - cs_s) = 2^(cs_l - cs_r0) 2^(cs_r0 - cs_s), both factors <= 1, so
-// nothing can overflow; diagonal tiles take the exact masked exponent.
+// tiles w and T-1-w (equal work per wave). x^T and h_prev (bf16) sit in LDS;
+// C rows and the precomputed CB tiles are read straight into registers, the
+// CB tile of the next step always in flight while the current one is used.
+// The mask M[l,s] = CB[l,s] 2^(cs_l - cs_s) dt_s is built in registers: for
+// off-diagonal tiles (j < i) the decay is split at the tile's first row r0,
+// 2^(cs_l - cs_r0) 2^(cs_r0 - cs_s), both factors <= 1, so nothing can
+// overflow; diagonal tiles take the exact masked exponent.
 // ============================================================================
 template <int N, int Q>
 __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
-  constexpr int T = Q / 32, NTHR = Q, KS = N / 32, PAIRS = T * (T + 1) / 2;
+  constexpr int T = Q / 32, NTHR = Q, PAIRS = T * (T + 1) / 2;
+  constexpr int HITEMS = kP * N / 8, HPER = (HITEMS + NTHR - 1) / NTHR;
   __shared__ __attribute__((aligned(16))) bf16 sX[kP * Q];
   __shared__ __attribute__((aligned(16))) bf16 sH[kP * N];
   __shared__ float sCs[Q];
@@ -241,139 +198,53 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
   if (!chunk_of(a, c, k)) return;
   const int h = blockIdx.y, g = h / a.heads_per_group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
-  const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
-  for (int l = tid; l < Q; l += NTHR) {
-    sCs[l] = cs[min(l, k.len - 1)];
-    sDt[l] = (l < k.len) ? (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + l) * a.H + h] : 0.f;
-  }
-  __syncthreads();
+
+  // Issue every global load of the staging phase first.
   const bf16 *xsrc = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
-  stage_transposed<kP, Q, NTHR>(sX, xsrc, (size_t)a.H * kP, 0, Q / 2, k.len, sDt);
+  Stager<kP, Q / 2, NTHR> sx;
+  sx.load(xsrc, (size_t)a.H * kP, 0, k.len);
+  const float *hp = a.states + ((size_t)c * a.H + h) * kP * N;
+  static_assert(HITEMS % NTHR == 0, "state staging must divide evenly");
+  float4 hv[HPER][2];
+#pragma unroll
+  for (int q = 0; q < HPER; ++q) {
+    const int it = tid + q * NTHR;
+    const int p = it / (N / 8), n8 = it - p * (N / 8);
+    hv[q][0] = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8);
+    hv[q][1] = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8 + 4);
+  }
+  const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
   {
-    const float *hp = a.states + ((size_t)c * a.H + h) * kP * N;
-    for (int it = tid; it < kP * N / 8; it += NTHR) {
-      const int p = it / (N / 8), n8 = it - p * (N / 8);
-      const float4 f0 = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8);
-      const float4 f1 = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8 + 4);
-      uint4 v;
-      v.x = pack2(f0.x, f0.y);
-      v.y = pack2(f0.z, f0.w);
-      v.z = pack2(f1.x, f1.y);
-      v.w = pack2(f1.z, f1.w);
-      *reinterpret_cast<uint4 *>(sH + swz<N>(p, 8 * n8)) = v;
-    }
+    const int l = tid, lc = min(l, k.len - 1);  // one token per thread (NTHR == Q)
+    const float cv = cs[lc];
+    const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h];
+    sCs[l] = cv;
+    sDt[l] = l < k.len ? d : 0.f;
+  }
+  sx.template store<Q>(sX, 0, nullptr);
+#pragma unroll
+  for (int q = 0; q < HPER; ++q) {
+    const int it = tid + q * NTHR;
+    const int p = it / (N / 8), n8 = it - p * (N / 8);
+    uint4 v;
+    v.x = pack2(hv[q][0].x, hv[q][0].y);
+    v.y = pack2(hv[q][0].z, hv[q][0].w);
+    v.z = pack2(hv[q][1].x, hv[q][1].y);
+    v.w = pack2(hv[q][1].z, hv[q][1].w);
+    *reinterpret_cast<uint4 *>(sH + swz<N>(p, 8 * n8)) = v;
   }
   __syncthreads();
 
   const bf16 *C = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
   const size_t ldc = (size_t)a.G * N;
-  const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512;
+  const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   const float dsk = a.D ? a.D[h] : 0.f;
-  const bf16 *xg = static_cast<const bf16 *>(a.x);
   bf16 *yg = static_cast<bf16 *>(a.y);
 
 #pragma unroll 1
-  for (int ti = 0; ti < 2; ++ti) {
-    const int i = ti == 0 ? wave : T - 1 - wave;
-    f32x4 Y[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // (a) state entering the chunk: C h_prev^T, then 2^(cs_l) per row.
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 ac[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = 32 * i + 16 * u + lr;
-        ac[u] = row < k.len ? ldg8(C + row * ldc + 32 * ks + 8 * lg) : zero8();
-      }
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(sH + swz<N>(16 * pt + lr, 32 * ks + 8 * lg));
-#pragma unroll
-        for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(ac[u], bh, Y[u][pt]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = exp2_fast(sCs[32 * i + 16 * u + 4 * lg + r]);
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) Y[u][pt][r] *= f;
-      }
-
-    // (b) intra-chunk tiles j <= i.
-    const float cs_r0 = sCs[32 * i];
-    float cs_row[2], rdec[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      cs_row[u] = sCs[32 * i + 16 * u + lr];
-      rdec[u] = exp2_fast(cs_row[u] - cs_r0);
-    }
-#pragma unroll 1
-    for (int j = 0; j <= i; ++j) {
-      const int pair = i * (i + 1) / 2 + j;
-      bf16x8 m[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) m[u] = ldg8(cbase + (size_t)(pair * 2 + u) * 512 + lane * 8);
-      if (j < i) {
-        float q[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          q[e] = exp2_fast(cs_r0 - sCs[32 * j + 16 * (e >> 2) + 4 * lg + (e & 3)]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) m[u][e] = (bf16)((float)m[u][e] * (rdec[u] * q[e]));
-      } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int l = 32 * i + 16 * u + lr;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int s = 32 * j + 16 * (e >> 2) + 4 * lg + (e & 3);
-            const float v = (float)m[u][e] * exp2_fast(cs_row[u] - sCs[s]);
-            m[u][e] = (bf16)(s <= l ? v : 0.f);
-          }
-        }
-      }
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int p = 16 * pt + lr;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(sX + swz<Q>(p, 32 * j + 4 * lg));
-        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(sX + swz<Q>(p, 32 * j + 16 + 4 * lg));
-        bf16x8 xv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xv[e] = lo[e];
-          xv[4 + e] = hi[e];
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(m[u], xv, Y[u][pt]);
-      }
-    }
-
-    // (c) skip term, round to bf16, store. Lane holds column p, 4 rows.
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int l = 32 * i + 16 * u + 4 * lg + r;
-        if (l < k.len) {
-          const size_t off = ((size_t)(k.start + l) * a.H + h) * kP;
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt) {
-            const int p = 16 * pt + lr;
-            yg[off + p] = (bf16)(Y[u][pt][r] + dsk * (float)xg[off + p]);
-          }
-        }
-      }
-  }
+  for (int ti = 0; ti < 2; ++ti)
+    chunk_rows_out<N, Q>(ti == 0 ? wave : T - 1 - wave, sX, sH, sCs, sDt, C, ldc, cbase,
+                         k.len, yg + ((size_t)k.start * a.H + h) * kP, (size_t)a.H * kP, dsk);
 }
 
 // ---- launchers ----------------------------------------------------------------

@@ -3,6 +3,11 @@
 //
 // Launch order on the caller's stream (one pass over the hot path):
 //   [varlen] k_plan            chunk table from cu_seqlens (device side)
+// then, by default for bf16 (chunk 128/256, P 64, N 64/128/256):
+//   k_chunk_cb                 C B^T once per (chunk, group)
+//   k_ssd_fused                one workgroup per (sequence, head) walks its
+//                              chunks with the state in registers
+// otherwise (fp32, other shapes, or SSD_FLAG_UNFUSED), one kernel per step:
 //   k_chunk_cumsum             log2-decay prefix inside each chunk
 //   k_chunk_state_{mfma,generic}  per-chunk states from a zero start
 //   k_state_passing            serial recurrence across chunks (in place)
@@ -37,20 +42,30 @@ ssd_status fail(ssd_status st, const char *fmt, ...) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Which kernels a problem runs on.
+enum Path {
+  kGeneric,      // plain FMA chunk kernels (fp32, and shapes MFMA does not cover)
+  kMfmaUnfused,  // one MFMA kernel per step of the method
+  kMfmaFused     // C B^T per (chunk, group) + one fused kernel per (sequence, head)
+};
+
 struct Layout {
   int64_t nc_max;
   int64_t rec_off;  // int32 offset of the chunk records in the plan area
   size_t plan, cs, states, cb, total;
+  Path path;
   bool mfma;
 };
 
-bool uses_mfma(const ssd_problem &p) {
-  if (p.dtype != SSD_DTYPE_BF16 || (p.flags & SSD_FLAG_GENERIC_KERNELS)) return false;
+Path path_of(const ssd_problem &p) {
+  if (p.dtype != SSD_DTYPE_BF16 || (p.flags & SSD_FLAG_GENERIC_KERNELS)) return kGeneric;
   ssd::Args a{};
   a.P = p.headdim;
   a.N = p.dstate;
   a.Q = p.chunk_size;
-  return ssd::mfma_path_supports(a);
+  if (!ssd::mfma_path_supports(a)) return kGeneric;
+  if ((p.flags & SSD_FLAG_UNFUSED) || !ssd::fused_path_supports(a)) return kMfmaUnfused;
+  return kMfmaFused;
 }
 
 Layout make_layout(const ssd_problem &p) {
@@ -60,14 +75,18 @@ Layout make_layout(const ssd_problem &p) {
                             : (int64_t)p.batch * ((p.seqlen + Q - 1) / Q);
   L.rec_off = p.num_seqs > 0 ? (int64_t)round_up(3 + (size_t)p.num_seqs, 4) : 0;
   const size_t plan_ints = p.num_seqs > 0 ? (size_t)(L.rec_off + 4 * L.nc_max) : 4;
-  L.mfma = uses_mfma(p);
+  L.path = path_of(p);
+  L.mfma = L.path != kGeneric;
+  const bool unfused = L.path != kMfmaFused;  // per-chunk intermediates in HBM
   size_t off = 0;
   L.plan = off;
   off = round_up(off + plan_ints * sizeof(int32_t), kAlign);
   L.cs = off;
-  off = round_up(off + (size_t)L.nc_max * p.nheads * Q * sizeof(float), kAlign);
+  if (unfused) off = round_up(off + (size_t)L.nc_max * p.nheads * Q * sizeof(float), kAlign);
   L.states = off;
-  off = round_up(off + (size_t)L.nc_max * p.nheads * p.headdim * p.dstate * sizeof(float), kAlign);
+  if (unfused)
+    off = round_up(off + (size_t)L.nc_max * p.nheads * p.headdim * p.dstate * sizeof(float),
+                   kAlign);
   L.cb = off;
   if (L.mfma) {
     const int64_t T = Q / 32;
@@ -150,6 +169,11 @@ struct StageNames {
 StageNames stage_names(const ssd::Args &a, const Layout &L, bool) {
   StageNames n{};
   if (a.varlen) n.name[n.count++] = "plan";
+  if (L.path == kMfmaFused) {
+    if (a.nc_max > 0) n.name[n.count++] = "chunk_cb";
+    n.name[n.count++] = "ssd_fused";
+    return n;
+  }
   if (a.nc_max > 0) {
     n.name[n.count++] = "chunk_cumsum";
     n.name[n.count++] = "chunk_state";
@@ -179,6 +203,11 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
   } while (0)
   if (!mark()) return fail(SSD_ERR_HIP, "hipEventRecord failed");
   if (a.varlen) SSD_LAUNCH(ssd::launch_plan(a, s), "plan");
+  if (L.path == kMfmaFused) {
+    if (a.nc_max > 0) SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
+    SSD_LAUNCH(ssd::launch_fused(a, a.cb, s), "ssd_fused");
+    return SSD_OK;
+  }
   if (a.nc_max > 0) {
     SSD_LAUNCH(ssd::launch_chunk_cumsum(a, bf, s), "chunk_cumsum");
     if (L.mfma)
@@ -232,7 +261,7 @@ ssd_status ssd_validate(const ssd_problem *p) {
   if (p->num_seqs > 0 && p->batch != 1)
     return fail(SSD_ERR_INVALID_ARG, "varlen (num_seqs %d) needs batch == 1, got %d",
                 p->num_seqs, p->batch);
-  if (p->flags & ~SSD_FLAG_GENERIC_KERNELS)
+  if (p->flags & ~(SSD_FLAG_GENERIC_KERNELS | SSD_FLAG_UNFUSED))
     return fail(SSD_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16)
     return fail(SSD_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);

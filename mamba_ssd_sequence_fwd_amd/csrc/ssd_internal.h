@@ -147,5 +147,7 @@ size_t cb_bytes(const Args &a);
 hipError_t launch_chunk_state_mfma(const Args &a, hipStream_t s);
 hipError_t launch_chunk_cb(const Args &a, void *cb, hipStream_t s);
 hipError_t launch_chunk_scan_mfma(const Args &a, const void *cb, hipStream_t s);
+bool fused_path_supports(const Args &a);
+hipError_t launch_fused(const Args &a, const void *cb, hipStream_t s);
 
 }  // namespace ssd

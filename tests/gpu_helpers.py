@@ -20,17 +20,17 @@ def to_device(inp: dict, dev="cuda") -> dict:
     return out
 
 
-def plan_for(inp: dict, chunk=None, generic=False, dev="cuda") -> ssd.Plan:
+def plan_for(inp: dict, chunk=None, generic=False, unfused=False, dev="cuda") -> ssd.Plan:
     d = to_device(inp, dev)
     w = inp["workload"]
     return ssd.Plan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
                     chunk_size=chunk or w.chunk, cu_seqlens=d["cu_seqlens"],
-                    generic=generic)
+                    generic=generic, unfused=unfused)
 
 
-def run_gpu(inp: dict, chunk=None, generic=False):
+def run_gpu(inp: dict, chunk=None, generic=False, unfused=False):
     """(y (T, H, P) fp64, final_state fp64, plan) after one ssd_forward."""
-    plan = plan_for(inp, chunk, generic)
+    plan = plan_for(inp, chunk, generic, unfused)
     print("[gpu] ssd_forward %s seed=%d %r" % (inp["workload"].name, inp["workload"].seed,
                                                plan.prob), flush=True)
     y, hT = plan.run()

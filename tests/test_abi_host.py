@@ -58,6 +58,7 @@ def status_of(fn, *a):
     ({"batch": 1, "num_seqs": 4}, ssd.SSD_OK),
     ({"seqlen": -1}, ssd.SSD_ERR_INVALID_ARG),
     ({"flags": 8}, ssd.SSD_ERR_INVALID_ARG),
+    ({"flags": ssd.SSD_FLAG_UNFUSED}, ssd.SSD_OK),
     ({"dtype": 7}, ssd.SSD_ERR_UNSUPPORTED),
     ({"headdim": 48}, ssd.SSD_ERR_UNSUPPORTED),
     ({"dstate": 24}, ssd.SSD_ERR_UNSUPPORTED),
@@ -88,7 +89,7 @@ def test_validate_cu_seqlens(lib, cu, status):
 
 
 def test_workspace_layout_dense(lib):
-    prob = P()
+    prob = P(flags=ssd.SSD_FLAG_UNFUSED)
     lay = ssd.workspace_layout(prob)
     nc = 2 * 4                                   # batch 2, ceil(1000/256) = 4
     assert lay.max_chunks == nc
@@ -109,8 +110,11 @@ def test_workspace_grows_with_problem(lib):
     a = ssd.workspace_size(P(seqlen=1000))
     b = ssd.workspace_size(P(seqlen=2000))
     assert b > a
-    # generic kernels need no C.B^T buffer
-    assert ssd.workspace_size(P(flags=ssd.SSD_FLAG_GENERIC_KERNELS)) < a
+    # generic kernels need no C.B^T buffer; the fused kernel keeps the
+    # per-chunk states on chip
+    unf = ssd.workspace_size(P(flags=ssd.SSD_FLAG_UNFUSED))
+    assert ssd.workspace_size(P(flags=ssd.SSD_FLAG_GENERIC_KERNELS)) < unf
+    assert a < unf
 
 
 def test_forward_rejects_bad_arguments_before_launch(lib):

@@ -68,6 +68,14 @@ def test_small_parity(case, small_inputs, small_oracle):
 
 
 @pytest.mark.parametrize("case", [k for k, w in SMALL.items() if w.dtype == "bf16"])
+def test_small_parity_unfused_kernels(case, small_inputs, small_oracle):
+    """One kernel per step (cumsum, chunk_state, state_passing, chunk_scan)."""
+    inp = small_inputs[case]
+    y, hT, _ = run_gpu(inp, unfused=True)
+    _compare(inp, (y, hT), small_oracle[case])
+
+
+@pytest.mark.parametrize("case", [k for k, w in SMALL.items() if w.dtype == "bf16"])
 def test_small_parity_generic_kernels(case, small_inputs, small_oracle):
     """The plain-FMA kernels on bf16 inputs (the MFMA path's fallback)."""
     inp = small_inputs[case]
@@ -75,11 +83,13 @@ def test_small_parity_generic_kernels(case, small_inputs, small_oracle):
     _compare(inp, (y, hT), small_oracle[case])
 
 
+@pytest.mark.parametrize("unfused", [False, True])
 @pytest.mark.parametrize("Q", [64, 128, 256])
-@pytest.mark.parametrize("case", ["cfg2-ragged-h0", "S1-slow-decay", "fp32-P64-N128"])
-def test_chunk_size_invariance(case, Q, small_inputs, small_oracle):
+@pytest.mark.parametrize("case", ["cfg2-ragged-h0", "S1-slow-decay", "fp32-P64-N128",
+                                  "cfg3-groups-N256", "bf16-N64"])
+def test_chunk_size_invariance(case, Q, unfused, small_inputs, small_oracle):
     inp = small_inputs[case]
-    y, hT, _ = run_gpu(inp, chunk=Q)
+    y, hT, _ = run_gpu(inp, chunk=Q, unfused=unfused)
     _compare(inp, (y, hT), small_oracle[case])
 
 
@@ -89,7 +99,7 @@ def test_intermediates(case, small_inputs):
     """Chunk log-decay prefix and the state entering every chunk."""
     inp = small_inputs[case]
     Q = inp["workload"].chunk
-    y, hT, plan = run_gpu(inp)
+    y, hT, plan = run_gpu(inp, unfused=True)
     lay = plan.layout()
     _, _, snaps = run_oracle(inp, snap_every=Q)
     nc = snaps.shape[0]
@@ -136,9 +146,10 @@ def test_empty_dense_batch_returns_initial_state():
     assert np.array_equal(hT, inp["h0"].double().numpy())
 
 
-def test_deterministic(small_inputs):
+@pytest.mark.parametrize("unfused", [False, True])
+def test_deterministic(small_inputs, unfused):
     inp = small_inputs["cfg2-ragged-h0"]
-    plan = plan_for(inp)
+    plan = plan_for(inp, unfused=unfused)
     y1, h1 = [t.clone() for t in plan.run()]
     y2, h2 = plan.run()
     torch.cuda.synchronize()
@@ -189,11 +200,12 @@ def _sample_pairs(nseq, H, rng, k=10):
     return sorted(pairs)
 
 
+@pytest.mark.parametrize("unfused", [False, True])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_full_workload_sampled(cfg):
+def test_full_workload_sampled(cfg, unfused):
     w = C[cfg]
     inp = si.make_inputs(w)
-    plan = plan_for(inp)
+    plan = plan_for(inp, unfused=unfused)
     print("[gpu] full workload %d %s %r" % (cfg, w.name, plan.prob), flush=True)
     y, hT = plan.run()
     torch.cuda.synchronize()
