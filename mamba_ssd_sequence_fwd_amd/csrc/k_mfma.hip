@@ -122,6 +122,8 @@ __global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
 template <int N, int Q>
 __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
   constexpr int T = Q / 32, KS = N / 32, PAIRS = T * (T + 1) / 2;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
+    reinterpret_cast<uint4 *>(a.zeros)[threadIdx.x] = make_uint4(0, 0, 0, 0);
   Chunk k;
   const int c = blockIdx.x;
   if (!chunk_of(a, c, k)) return;
@@ -188,11 +190,13 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
 template <int N, int Q>
 __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
   constexpr int T = Q / 32, NTHR = Q, PAIRS = T * (T + 1) / 2;
-  constexpr int HITEMS = kP * N / 8, HPER = (HITEMS + NTHR - 1) / NTHR;
-  __shared__ __attribute__((aligned(16))) bf16 sX[kP * Q];
+  constexpr int HITEMS = kP * N / 8, HPER = HITEMS / NTHR;
+  static_assert(HITEMS % NTHR == 0, "state staging must divide evenly");
+  __shared__ __attribute__((aligned(16))) bf16 sX[Q * kP];
   __shared__ __attribute__((aligned(16))) bf16 sH[kP * N];
-  __shared__ float sCs[Q];
-  __shared__ float sDt[Q];
+  __shared__ __attribute__((aligned(16))) float sCs[Q];
+  __shared__ __attribute__((aligned(16))) float sDt[Q];
+  __shared__ __attribute__((aligned(16))) float sU[Q];
   Chunk k;
   const int c = blockIdx.x;
   if (!chunk_of(a, c, k)) return;
@@ -201,10 +205,9 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
 
   // Issue every global load of the staging phase first.
   const bf16 *xsrc = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
-  Stager<kP, Q / 2, NTHR> sx;
+  RowStager<kP, Q, NTHR> sx;
   sx.load(xsrc, (size_t)a.H * kP, 0, k.len);
   const float *hp = a.states + ((size_t)c * a.H + h) * kP * N;
-  static_assert(HITEMS % NTHR == 0, "state staging must divide evenly");
   float4 hv[HPER][2];
 #pragma unroll
   for (int q = 0; q < HPER; ++q) {
@@ -214,14 +217,15 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
     hv[q][1] = *reinterpret_cast<const float4 *>(hp + p * N + 8 * n8 + 4);
   }
   const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
-  {
-    const int l = tid, lc = min(l, k.len - 1);  // one token per thread (NTHR == Q)
-    const float cv = cs[lc];
-    const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h];
-    sCs[l] = cv;
-    sDt[l] = l < k.len ? d : 0.f;
-  }
-  sx.template store<Q>(sX, 0, nullptr);
+  const int lc = min(tid, k.len - 1);  // one token per thread (NTHR == Q)
+  const float cst = cs[lc];
+  const float cse = cs[min(tid | 31, k.len - 1)];
+  const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h];
+  const float dtv = tid < k.len ? d : 0.f;
+  sCs[tid] = cst;
+  sDt[tid] = dtv;
+  sU[tid] = exp2_fast(cse - cst) * dtv;
+  sx.store(sX);
 #pragma unroll
   for (int q = 0; q < HPER; ++q) {
     const int it = tid + q * NTHR;
@@ -240,10 +244,9 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
   const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   const float dsk = a.D ? a.D[h] : 0.f;
   bf16 *yg = static_cast<bf16 *>(a.y);
-
 #pragma unroll 1
   for (int ti = 0; ti < 2; ++ti)
-    chunk_rows_out<N, Q>(ti == 0 ? wave : T - 1 - wave, sX, sH, sCs, sDt, C, ldc, cbase,
+    chunk_rows_out<N, Q>(ti == 0 ? wave : T - 1 - wave, sX, sH, sCs, sDt, sU, C, ldc, cbase,
                          k.len, yg + ((size_t)k.start * a.H + h) * kP, (size_t)a.H * kP, dsk);
 }
 

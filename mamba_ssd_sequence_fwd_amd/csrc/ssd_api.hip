@@ -52,7 +52,7 @@ enum Path {
 struct Layout {
   int64_t nc_max;
   int64_t rec_off;  // int32 offset of the chunk records in the plan area
-  size_t plan, cs, states, cb, total;
+  size_t plan, cs, states, cb, zeros, total;
   Path path;
   bool mfma;
 };
@@ -92,6 +92,8 @@ Layout make_layout(const ssd_problem &p) {
     const int64_t T = Q / 32;
     off = round_up(off + (size_t)L.nc_max * p.ngroups * (T * (T + 1) / 2) * 2 * 1024, kAlign);
   }
+  L.zeros = off;
+  if (L.mfma) off += kAlign;
   L.total = off;
   return L;
 }
@@ -145,6 +147,7 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.cs = reinterpret_cast<float *>(ws + L.cs);
   a.states = reinterpret_cast<float *>(ws + L.states);
   a.cb = ws + L.cb;
+  a.zeros = ws + L.zeros;
   a.batch = p->batch;
   a.L = p->seqlen;
   a.H = p->nheads;
@@ -205,7 +208,7 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
   if (a.varlen) SSD_LAUNCH(ssd::launch_plan(a, s), "plan");
   if (L.path == kMfmaFused) {
     if (a.nc_max > 0) SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
-    SSD_LAUNCH(ssd::launch_fused(a, a.cb, s), "ssd_fused");
+    SSD_LAUNCH(ssd::launch_fused(a, a.cb, a.zeros, s), "ssd_fused");
     return SSD_OK;
   }
   if (a.nc_max > 0) {

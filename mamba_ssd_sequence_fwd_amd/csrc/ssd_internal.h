@@ -26,6 +26,7 @@ struct Args {
   float *cs;            // (chunks, H, Q): log2 decay prefix inside the chunk
   float *states;        // (chunks, H, P, N)
   void *cb;             // bf16 C B^T tiles (MFMA path only)
+  void *zeros;          // 256 zero bytes (written by the C B^T kernel)
   int32_t batch, L, H, P, N, G, Q;
   int32_t nseq;         // sequences: batch (dense) or num_seqs (varlen)
   int32_t varlen;       // 0 / 1
@@ -148,6 +149,6 @@ hipError_t launch_chunk_state_mfma(const Args &a, hipStream_t s);
 hipError_t launch_chunk_cb(const Args &a, void *cb, hipStream_t s);
 hipError_t launch_chunk_scan_mfma(const Args &a, const void *cb, hipStream_t s);
 bool fused_path_supports(const Args &a);
-hipError_t launch_fused(const Args &a, const void *cb, hipStream_t s);
+hipError_t launch_fused(const Args &a, const void *cb, const void *zeros, hipStream_t s);
 
 }  // namespace ssd
