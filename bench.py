@@ -67,6 +67,11 @@ def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
         bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + causal * G * 2 + S * H * state * (
             2 if inp["h0"] is not None else 1),
         flops=2 * causal * H * P + 4 * T * H * N * P + 2 * nc * H * P * N)
+    # chained kernel: the fused minimum plus the fp32 state hand-off between
+    # consecutive chunks of a sequence (written once, read once)
+    handoff = 2 * (nc - S) * H * state
+    cost["ssd_chain"] = dict(bytes=cost["ssd_fused"]["bytes"] + handoff,
+                             flops=cost["ssd_fused"]["flops"])
     cost["_path"] = dict(
         bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + S * H * state * (
             2 if inp["h0"] is not None else 1),
@@ -123,6 +128,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
                     help="run one kernel per step of the method instead of the fused kernel")
+    ap.add_argument("--per-sequence", action="store_true",
+                    help="run the fused kernel with one workgroup per (sequence, head)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy "
@@ -154,7 +161,8 @@ def main():
     d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("x", "dt", "A", "B", "C",
                                                                    "D", "h0")}
     plan = ssd.Plan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
-                    chunk_size=w.chunk, cu_seqlens=inp["cu_seqlens"], unfused=args.unfused)
+                    chunk_size=w.chunk, cu_seqlens=inp["cu_seqlens"], unfused=args.unfused,
+                    per_sequence=args.per_sequence)
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         plan.run(stream)
@@ -194,7 +202,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "fp32", "data": "synthetic",
-        "config": {"workload": w.name, "kernels": "unfused" if args.unfused else "default", "batch": w.batch if not w.num_seqs else 1,
+        "config": {"workload": w.name, "kernels": ("unfused" if args.unfused else
+                                                     "per_sequence" if args.per_sequence else
+                                                     "default"), "batch": w.batch if not w.num_seqs else 1,
                    "seq_len": plan.prob.seqlen, "nheads": w.nheads, "headdim": w.headdim,
                    "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk,
                    "num_seqs": w.num_seqs, "tokens_per_step": tokens,

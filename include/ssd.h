@@ -66,6 +66,11 @@ typedef enum ssd_dtype {
                                        the workspace, instead of the fused
                                        kernel that bf16 problems use by
                                        default */
+#define SSD_FLAG_PER_SEQUENCE 4u    /* fused kernel with one workgroup per
+                                       (sequence, head) walking its chunks in
+                                       order, instead of the default one
+                                       workgroup per (chunk, head) chained
+                                       through the state hand-off */
 
 /*
  * Problem description.
@@ -195,6 +200,11 @@ typedef struct ssd_workspace_layout {
   size_t chunk_table;
   int64_t chunk_records;
   int64_t max_chunks;
+  size_t chain_sync;        /* int32 words of the chained kernel: [1] is
+                               nonzero after a pass in which a workgroup
+                               gave up waiting for its predecessor's state
+                               (outputs then wrong); 0 = no chained kernel */
+  int64_t chain_sync_words; /* number of those words (0 = none) */
 } ssd_workspace_layout;
 ssd_status ssd_get_workspace_layout(const ssd_problem *prob,
                                     ssd_workspace_layout *layout);

@@ -10,6 +10,7 @@ with ``python -m mamba_ssd_sequence_fwd_amd.build``.
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, Plan, Problem, SSDError, StageTimes, WorkspaceLayout, forward, load,
     make_problem, validate, validate_cu_seqlens, workspace_layout, workspace_size,
-    SSD_DTYPE_BF16, SSD_DTYPE_F32, SSD_FLAG_GENERIC_KERNELS, SSD_FLAG_UNFUSED, SSD_OK,
+    SSD_DTYPE_BF16, SSD_DTYPE_F32, SSD_FLAG_GENERIC_KERNELS, SSD_FLAG_UNFUSED, SSD_FLAG_PER_SEQUENCE,
+    SSD_OK,
     SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP,
 )

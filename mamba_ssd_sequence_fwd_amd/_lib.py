@@ -20,6 +20,7 @@ SSD_OK, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED, SSD_ERR_WORKSPACE, SSD_ERR_HIP
 SSD_DTYPE_F32, SSD_DTYPE_BF16 = 0, 1
 SSD_FLAG_GENERIC_KERNELS = 1
 SSD_FLAG_UNFUSED = 2
+SSD_FLAG_PER_SEQUENCE = 4
 
 
 class SSDError(RuntimeError):
@@ -42,7 +43,8 @@ class Problem(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("chunk_cumsum", ctypes.c_size_t), ("chunk_states", ctypes.c_size_t),
                 ("chunk_table", ctypes.c_size_t), ("chunk_records", ctypes.c_int64),
-                ("max_chunks", ctypes.c_int64)]
+                ("max_chunks", ctypes.c_int64), ("chain_sync", ctypes.c_size_t),
+                ("chain_sync_words", ctypes.c_int64)]
 
 
 MAX_STAGES = 8
@@ -160,7 +162,7 @@ class Plan:
 
     def __init__(self, x, dt, A, B, C, D=None, initial_state=None, chunk_size=256,
                  cu_seqlens=None, *, want_final_state=True, generic=False,
-                 unfused=False, check_cu_seqlens=True):
+                 unfused=False, per_sequence=False, check_cu_seqlens=True):
         if x.dim() != 4:
             raise ValueError("x must be (batch, seqlen, nheads, headdim)")
         batch, L, H, P = x.shape
@@ -192,7 +194,8 @@ class Plan:
         self.prob = make_problem(batch, L, H, P, N, G, chunk_size, num_seqs,
                                  _DTYPES[x.dtype],
                                  (SSD_FLAG_GENERIC_KERNELS if generic else 0)
-                                 | (SSD_FLAG_UNFUSED if unfused else 0))
+                                 | (SSD_FLAG_UNFUSED if unfused else 0)
+                                 | (SSD_FLAG_PER_SEQUENCE if per_sequence else 0))
         validate(self.prob)
         if cu_seqlens is not None:
             if check_cu_seqlens or cu_seqlens.device.type == "cpu":
@@ -237,6 +240,17 @@ class Plan:
 
     def layout(self) -> WorkspaceLayout:
         return workspace_layout(self.prob)
+
+    def chain_error(self) -> int:
+        """Error word of the chained kernel after the passes run so far
+        (synchronises): nonzero if a workgroup gave up waiting for its
+        predecessor's state. 0 when the problem does not use that kernel."""
+        lay = self.layout()
+        if lay.chain_sync_words == 0:
+            return 0
+        torch.cuda.synchronize(self.workspace.device)
+        w = self.workspace[lay.chain_sync:lay.chain_sync + 8].view(torch.int32)
+        return int(w[1].item())
 
 
 def forward(x, dt, A, B, C, D=None, initial_state=None, chunk_size=256, cu_seqlens=None,

@@ -124,6 +124,13 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
   constexpr int T = Q / 32, KS = N / 32, PAIRS = T * (T + 1) / 2;
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
     reinterpret_cast<uint4 *>(a.zeros)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+  {
+    // Chain path: clear the ticket, error word and published-chunk counters
+    // for the kernel that follows on the stream.
+    const int nb = gridDim.x * gridDim.y * gridDim.z;
+    const int b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    for (int i = b * 64 + threadIdx.x; i < a.nsync; i += nb * 64) a.sync[i] = 0;
+  }
   Chunk k;
   const int c = blockIdx.x;
   if (!chunk_of(a, c, k)) return;

@@ -4,8 +4,12 @@
 // Launch order on the caller's stream (one pass over the hot path):
 //   [varlen] k_plan            chunk table from cu_seqlens (device side)
 // then, by default for bf16 (chunk 128/256, P 64, N 64/128/256):
-//   k_chunk_cb                 C B^T once per (chunk, group)
-//   k_ssd_fused                one workgroup per (sequence, head) walks its
+//   k_chunk_cb                 C B^T once per (chunk, group); clears the
+//                              chain counters
+//   k_ssd_chain                one workgroup per (chunk, head); the state
+//                              recurrence handed from chunk to chunk
+// or, with SSD_FLAG_PER_SEQUENCE,
+//   k_chunk_cb, k_ssd_fused    one workgroup per (sequence, head) walks its
 //                              chunks with the state in registers
 // otherwise (fp32, other shapes, or SSD_FLAG_UNFUSED), one kernel per step:
 //   k_chunk_cumsum             log2-decay prefix inside each chunk
@@ -46,13 +50,15 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 enum Path {
   kGeneric,      // plain FMA chunk kernels (fp32, and shapes MFMA does not cover)
   kMfmaUnfused,  // one MFMA kernel per step of the method
-  kMfmaFused     // C B^T per (chunk, group) + one fused kernel per (sequence, head)
+  kMfmaFused,    // C B^T per (chunk, group) + one fused kernel per (sequence, head)
+  kMfmaChain     // C B^T per (chunk, group) + one workgroup per (chunk, head), chained
 };
 
 struct Layout {
   int64_t nc_max;
   int64_t rec_off;  // int32 offset of the chunk records in the plan area
-  size_t plan, cs, states, cb, zeros, total;
+  size_t plan, cs, states, cb, zeros, sync, ring, total;
+  int64_t nsync;
   Path path;
   bool mfma;
 };
@@ -64,8 +70,10 @@ Path path_of(const ssd_problem &p) {
   a.N = p.dstate;
   a.Q = p.chunk_size;
   if (!ssd::mfma_path_supports(a)) return kGeneric;
-  if ((p.flags & SSD_FLAG_UNFUSED) || !ssd::fused_path_supports(a)) return kMfmaUnfused;
-  return kMfmaFused;
+  if (p.flags & SSD_FLAG_UNFUSED) return kMfmaUnfused;
+  if (p.flags & SSD_FLAG_PER_SEQUENCE)
+    return ssd::fused_path_supports(a) ? kMfmaFused : kMfmaUnfused;
+  return ssd::chain_path_supports(a) ? kMfmaChain : kMfmaUnfused;
 }
 
 Layout make_layout(const ssd_problem &p) {
@@ -77,7 +85,7 @@ Layout make_layout(const ssd_problem &p) {
   const size_t plan_ints = p.num_seqs > 0 ? (size_t)(L.rec_off + 4 * L.nc_max) : 4;
   L.path = path_of(p);
   L.mfma = L.path != kGeneric;
-  const bool unfused = L.path != kMfmaFused;  // per-chunk intermediates in HBM
+  const bool unfused = L.path == kGeneric || L.path == kMfmaUnfused;  // per-chunk intermediates
   size_t off = 0;
   L.plan = off;
   off = round_up(off + plan_ints * sizeof(int32_t), kAlign);
@@ -94,6 +102,14 @@ Layout make_layout(const ssd_problem &p) {
   }
   L.zeros = off;
   if (L.mfma) off += kAlign;
+  const int64_t nseq = p.num_seqs > 0 ? p.num_seqs : p.batch;
+  L.sync = off;
+  L.nsync = (L.path == kMfmaChain && L.nc_max > 0) ? ssd::kSyncHeader + nseq * p.nheads : 0;
+  off = round_up(off + (size_t)L.nsync * sizeof(int32_t), kAlign);
+  L.ring = off;
+  if (L.nsync > 0)
+    off = round_up(off + (size_t)nseq * p.nheads * 2 * p.headdim * p.dstate * sizeof(float),
+                   kAlign);
   L.total = off;
   return L;
 }
@@ -148,6 +164,9 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.states = reinterpret_cast<float *>(ws + L.states);
   a.cb = ws + L.cb;
   a.zeros = ws + L.zeros;
+  a.sync = reinterpret_cast<int32_t *>(ws + L.sync);
+  a.ring = reinterpret_cast<float *>(ws + L.ring);
+  a.nsync = (int32_t)L.nsync;
   a.batch = p->batch;
   a.L = p->seqlen;
   a.H = p->nheads;
@@ -164,6 +183,13 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   return a;
 }
 
+// Sequences without tokens get no chunk workgroup on the chain path; their
+// final states (initial state or zeros) come from a separate small pass.
+// Only varlen problems and empty dense batches can have such sequences.
+bool chain_needs_empty_pass(const ssd::Args &a) {
+  return a.hT != nullptr && (a.varlen || a.L == 0);
+}
+
 struct StageNames {
   int count;
   const char *name[SSD_MAX_STAGES];
@@ -175,6 +201,14 @@ StageNames stage_names(const ssd::Args &a, const Layout &L, bool) {
   if (L.path == kMfmaFused) {
     if (a.nc_max > 0) n.name[n.count++] = "chunk_cb";
     n.name[n.count++] = "ssd_fused";
+    return n;
+  }
+  if (L.path == kMfmaChain) {
+    if (a.nc_max > 0) {
+      n.name[n.count++] = "chunk_cb";
+      n.name[n.count++] = "ssd_chain";
+    }
+    if (chain_needs_empty_pass(a)) n.name[n.count++] = "final_of_empty";
     return n;
   }
   if (a.nc_max > 0) {
@@ -209,6 +243,15 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
   if (L.path == kMfmaFused) {
     if (a.nc_max > 0) SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
     SSD_LAUNCH(ssd::launch_fused(a, a.cb, a.zeros, s), "ssd_fused");
+    return SSD_OK;
+  }
+  if (L.path == kMfmaChain) {
+    if (a.nc_max > 0) {
+      SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
+      SSD_LAUNCH(ssd::launch_chain(a, a.cb, a.zeros, s), "ssd_chain");
+    }
+    if (chain_needs_empty_pass(a))
+      SSD_LAUNCH(ssd::launch_final_of_empty(a, s), "final_of_empty");
     return SSD_OK;
   }
   if (a.nc_max > 0) {
@@ -264,7 +307,7 @@ ssd_status ssd_validate(const ssd_problem *p) {
   if (p->num_seqs > 0 && p->batch != 1)
     return fail(SSD_ERR_INVALID_ARG, "varlen (num_seqs %d) needs batch == 1, got %d",
                 p->num_seqs, p->batch);
-  if (p->flags & ~(SSD_FLAG_GENERIC_KERNELS | SSD_FLAG_UNFUSED))
+  if (p->flags & ~(SSD_FLAG_GENERIC_KERNELS | SSD_FLAG_UNFUSED | SSD_FLAG_PER_SEQUENCE))
     return fail(SSD_ERR_INVALID_ARG, "unknown flags 0x%x", p->flags);
   if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16)
     return fail(SSD_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
@@ -323,6 +366,8 @@ ssd_status ssd_get_workspace_layout(const ssd_problem *p, ssd_workspace_layout *
   out->chunk_table = L.plan;
   out->chunk_records = L.rec_off;
   out->max_chunks = L.nc_max;
+  out->chain_sync = L.nsync ? L.sync : 0;
+  out->chain_sync_words = L.nsync;
   return SSD_OK;
 }
 

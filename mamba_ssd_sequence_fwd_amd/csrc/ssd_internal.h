@@ -27,6 +27,10 @@ struct Args {
   float *states;        // (chunks, H, P, N)
   void *cb;             // bf16 C B^T tiles (MFMA path only)
   void *zeros;          // 256 zero bytes (written by the C B^T kernel)
+  int32_t *sync;        // chain path: [0] ticket, [1] error word, [kSyncHeader + seq*H + h]
+                        // published-chunk counters; zeroed by the C B^T kernel
+  float *ring;          // chain path: (S, H, 2, P, N) fp32 state hand-off ring
+  int32_t nsync;        // ints of `sync` to zero (0 off the chain path)
   int32_t batch, L, H, P, N, G, Q;
   int32_t nseq;         // sequences: batch (dense) or num_seqs (varlen)
   int32_t varlen;       // 0 / 1
@@ -35,6 +39,9 @@ struct Args {
   int32_t heads_per_group;
   int32_t rec_off;      // int offset of the chunk records inside plan
 };
+
+// Ints ahead of the per-(sequence, head) counters in Args::sync.
+constexpr int kSyncHeader = 64;
 
 // Chunk c's place in the token stream.
 struct Chunk {
@@ -150,5 +157,8 @@ hipError_t launch_chunk_cb(const Args &a, void *cb, hipStream_t s);
 hipError_t launch_chunk_scan_mfma(const Args &a, const void *cb, hipStream_t s);
 bool fused_path_supports(const Args &a);
 hipError_t launch_fused(const Args &a, const void *cb, const void *zeros, hipStream_t s);
+bool chain_path_supports(const Args &a);
+hipError_t launch_chain(const Args &a, const void *cb, const void *zeros, hipStream_t s);
+hipError_t launch_final_of_empty(const Args &a, hipStream_t s);
 
 }  // namespace ssd

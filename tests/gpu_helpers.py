@@ -20,21 +20,29 @@ def to_device(inp: dict, dev="cuda") -> dict:
     return out
 
 
-def plan_for(inp: dict, chunk=None, generic=False, unfused=False, dev="cuda") -> ssd.Plan:
+# Kernel paths of the library: the default (chained per-(chunk, head)
+# workgroups for bf16), the per-(sequence, head) fused kernel, and one kernel
+# per step of the method.
+PATHS = {"default": {}, "per_sequence": {"per_sequence": True}, "unfused": {"unfused": True}}
+
+
+def plan_for(inp: dict, chunk=None, generic=False, unfused=False, per_sequence=False,
+             dev="cuda") -> ssd.Plan:
     d = to_device(inp, dev)
     w = inp["workload"]
     return ssd.Plan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
                     chunk_size=chunk or w.chunk, cu_seqlens=d["cu_seqlens"],
-                    generic=generic, unfused=unfused)
+                    generic=generic, unfused=unfused, per_sequence=per_sequence)
 
 
-def run_gpu(inp: dict, chunk=None, generic=False, unfused=False):
+def run_gpu(inp: dict, chunk=None, generic=False, unfused=False, per_sequence=False):
     """(y (T, H, P) fp64, final_state fp64, plan) after one ssd_forward."""
-    plan = plan_for(inp, chunk, generic, unfused)
+    plan = plan_for(inp, chunk, generic, unfused, per_sequence)
     print("[gpu] ssd_forward %s seed=%d %r" % (inp["workload"].name, inp["workload"].seed,
                                                plan.prob), flush=True)
     y, hT = plan.run()
     torch.cuda.synchronize()
+    assert plan.chain_error() == 0, "a chained workgroup timed out waiting for its state"
     T = plan.tokens
     y64 = y.reshape(T, y.shape[2], y.shape[3]).to(torch.float64).cpu().numpy()
     return y64, hT.to(torch.float64).cpu().numpy(), plan

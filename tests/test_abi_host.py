@@ -59,6 +59,7 @@ def status_of(fn, *a):
     ({"seqlen": -1}, ssd.SSD_ERR_INVALID_ARG),
     ({"flags": 8}, ssd.SSD_ERR_INVALID_ARG),
     ({"flags": ssd.SSD_FLAG_UNFUSED}, ssd.SSD_OK),
+    ({"flags": ssd.SSD_FLAG_PER_SEQUENCE}, ssd.SSD_OK),
     ({"dtype": 7}, ssd.SSD_ERR_UNSUPPORTED),
     ({"headdim": 48}, ssd.SSD_ERR_UNSUPPORTED),
     ({"dstate": 24}, ssd.SSD_ERR_UNSUPPORTED),
@@ -104,6 +105,19 @@ def test_workspace_layout_varlen_bound(lib):
     lay = ssd.workspace_layout(prob)
     assert lay.max_chunks == 5000 // 256 + 7
     assert lay.chunk_records >= 3 + 7 and lay.chunk_records % 4 == 0
+
+
+def test_workspace_layout_chain_counters(lib):
+    """The default bf16 path (chained workgroups) has one counter per
+    (sequence, head) after a 64-word header; the other paths have none."""
+    lay = ssd.workspace_layout(P())
+    assert lay.chain_sync_words == 64 + 2 * 8 and lay.chain_sync % 256 == 0
+    assert ssd.workspace_size(P()) >= lay.chain_sync + 4 * lay.chain_sync_words + \
+        2 * 8 * 2 * 64 * 128 * 4
+    lay_v = ssd.workspace_layout(P(batch=1, seqlen=5000, num_seqs=7))
+    assert lay_v.chain_sync_words == 64 + 7 * 8
+    for flags in (ssd.SSD_FLAG_UNFUSED, ssd.SSD_FLAG_PER_SEQUENCE, ssd.SSD_FLAG_GENERIC_KERNELS):
+        assert ssd.workspace_layout(P(flags=flags)).chain_sync_words == 0
 
 
 def test_workspace_grows_with_problem(lib):

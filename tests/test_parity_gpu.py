@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import ssd_inputs as si
-from gpu_helpers import (flat_inputs, plan_for, rel_err, run_gpu, run_oracle,
+from gpu_helpers import (PATHS, flat_inputs, plan_for, rel_err, run_gpu, run_oracle,
                          seq_lens_of, tol_of)
 
 pytestmark = pytest.mark.gpu
@@ -76,6 +76,13 @@ def test_small_parity_unfused_kernels(case, small_inputs, small_oracle):
 
 
 @pytest.mark.parametrize("case", [k for k, w in SMALL.items() if w.dtype == "bf16"])
+def test_small_parity_per_sequence_kernel(case, small_inputs, small_oracle):
+    inp = small_inputs[case]
+    y, hT, _ = run_gpu(inp, per_sequence=True)
+    _compare(inp, (y, hT), small_oracle[case])
+
+
+@pytest.mark.parametrize("case", [k for k, w in SMALL.items() if w.dtype == "bf16"])
 def test_small_parity_generic_kernels(case, small_inputs, small_oracle):
     """The plain-FMA kernels on bf16 inputs (the MFMA path's fallback)."""
     inp = small_inputs[case]
@@ -83,13 +90,13 @@ def test_small_parity_generic_kernels(case, small_inputs, small_oracle):
     _compare(inp, (y, hT), small_oracle[case])
 
 
-@pytest.mark.parametrize("unfused", [False, True])
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("Q", [64, 128, 256])
 @pytest.mark.parametrize("case", ["cfg2-ragged-h0", "S1-slow-decay", "fp32-P64-N128",
                                   "cfg3-groups-N256", "bf16-N64"])
-def test_chunk_size_invariance(case, Q, unfused, small_inputs, small_oracle):
+def test_chunk_size_invariance(case, Q, path, small_inputs, small_oracle):
     inp = small_inputs[case]
-    y, hT, _ = run_gpu(inp, chunk=Q, unfused=unfused)
+    y, hT, _ = run_gpu(inp, chunk=Q, **PATHS[path])
     _compare(inp, (y, hT), small_oracle[case])
 
 
@@ -146,10 +153,10 @@ def test_empty_dense_batch_returns_initial_state():
     assert np.array_equal(hT, inp["h0"].double().numpy())
 
 
-@pytest.mark.parametrize("unfused", [False, True])
-def test_deterministic(small_inputs, unfused):
+@pytest.mark.parametrize("path", list(PATHS))
+def test_deterministic(small_inputs, path):
     inp = small_inputs["cfg2-ragged-h0"]
-    plan = plan_for(inp, unfused=unfused)
+    plan = plan_for(inp, **PATHS[path])
     y1, h1 = [t.clone() for t in plan.run()]
     y2, h2 = plan.run()
     torch.cuda.synchronize()
@@ -200,15 +207,16 @@ def _sample_pairs(nseq, H, rng, k=10):
     return sorted(pairs)
 
 
-@pytest.mark.parametrize("unfused", [False, True])
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
-def test_full_workload_sampled(cfg, unfused):
+def test_full_workload_sampled(cfg, path):
     w = C[cfg]
     inp = si.make_inputs(w)
-    plan = plan_for(inp, unfused=unfused)
+    plan = plan_for(inp, **PATHS[path])
     print("[gpu] full workload %d %s %r" % (cfg, w.name, plan.prob), flush=True)
     y, hT = plan.run()
     torch.cuda.synchronize()
+    assert plan.chain_error() == 0
     assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(hT).all())
     lens = seq_lens_of(inp)
     starts = np.concatenate([[0], np.cumsum(lens)])
