@@ -25,13 +25,15 @@
 //      published (the state_passing step).
 //   5. outputs += 2^(cs_l) C_l h_in^T (the rest of the chunk_scan step); y.
 //
-// Steps 2-3 need nothing from other workgroups, so the wait in step 4 is
-// normally already satisfied: the predecessor took its ticket H tickets
-// earlier. Tickets are handed out in (chunk, head) order by an atomic
-// counter, so a workgroup only ever waits on one that is already running:
-// the chain cannot deadlock whatever order the hardware dispatches in. Every
-// wait is bounded by a wall-clock limit; a wait that runs out sets an error
-// word instead of hanging (and the outputs are then wrong).
+// Steps 2-3 need nothing from other workgroups. Tickets from an atomic
+// counter order the work units by chunk index inside the sequence, then
+// sequence, then head, so the predecessor of a unit took its ticket a whole
+// chunk-index level earlier and has normally published by the time step 4
+// asks. A workgroup only ever waits on a smaller ticket, i.e. on one that is
+// already running, so the chain cannot deadlock whatever order the hardware
+// dispatches in. Every wait is bounded by a wall-clock limit; a wait that
+// runs out sets an error word instead of hanging (the outputs are then
+// wrong).
 //
 // HBM traffic: x, y once; B, C, dt and the C B^T tiles once per head
 // through L2; 32 KB of fp32 state written and read per (chunk, head).
@@ -209,21 +211,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (tid == 0) sTicket = atomicAdd(ticket, 1);
   __syncthreads();
   const int tk = sTicket;
-  // Ticket order: dense batches go chunk index by chunk index across all
-  // sequences (all first chunks, then all second chunks, ...), so a chunk's
-  // predecessor is nseq * H tickets back and has usually finished by then.
+  // Ticket order: chunk index by chunk index across all sequences (all first
+  // chunks, then all second chunks, ...), so a chunk's predecessor is many
+  // tickets back and has usually finished by then.
   int c, h;
   if (!a.varlen) {
     const int per = a.nseq * a.H;
     const int j = tk / per, r = tk - j * per, s = r / a.H;
     h = r - s * a.H;
     c = s * a.nc_per + j;
-  } else {
-    c = tk / a.H;
-    h = tk - c * a.H;
+  } else {  // chunk order of the plan (by index inside the sequence)
+    const int kk = tk / a.H;
+    h = tk - kk * a.H;
+    if (kk >= a.plan[0]) return;  // unused chunk slot: uniform per workgroup
+    c = a.plan[a.order_off + kk];
   }
   Chunk k;
-  if (!chunk_of(a, c, k)) return;  // unused chunk slot (varlen): uniform per workgroup
+  if (!chunk_of(a, c, k)) return;
   const int g = h / a.heads_per_group;
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N;
   const bf16 *xc = static_cast<const bf16 *>(a.x) + (size_t)k.start * ldx + (size_t)h * kP;

@@ -13,10 +13,13 @@
 namespace ssd {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kOrderMaxSeqs = 4096;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   __shared__ int s_wave_tot[kPlanThreads / 64];
   __shared__ int s_bad;
+  __shared__ int s_first[kOrderMaxSeqs];
+  __shared__ int s_nch[kOrderMaxSeqs];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.nseq, Q = a.Q;
   int *first = a.plan + 2;  // first chunk of each sequence, then the total
@@ -59,6 +62,37 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
     const int lo = a.cu[s], len = a.cu[s + 1] - lo, c0 = first[s];
     for (int i = 0, off = 0; off < len; ++i, off += Q)
       rec[c0 + i] = make_int4(s, lo + off, min(Q, len - off), i);
+  }
+  // Chunk order for the chained kernel: by index inside the sequence, then
+  // by sequence (all first chunks, then all second chunks, ...), so that a
+  // chunk comes long after its predecessor. Chunk i of sequence s goes to
+  // position sum_s' min(chunks(s'), i) + #{s' < s : chunks(s') > i}; with
+  // more than kOrderMaxSeqs sequences the sequence-major order is kept.
+  int *order = a.plan + a.order_off;
+  const int nc = carry;
+  if (S > kOrderMaxSeqs) {
+    for (int c = tid; c < nc; c += kPlanThreads) order[c] = c;
+    return;
+  }
+  for (int s = tid; s < S; s += kPlanThreads) {
+    s_first[s] = first[s];
+    s_nch[s] = (a.cu[s + 1] - a.cu[s] + Q - 1) / Q;
+  }
+  __syncthreads();
+  for (int c = tid; c < nc; c += kPlanThreads) {
+    int lo = 0, hi = S - 1;  // last sequence whose first chunk is <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    const int i = c - s_first[lo];
+    int pos = 0;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int n2 = s_nch[s2];
+      pos += min(n2, i) + ((s2 < lo && n2 > i) ? 1 : 0);
+    }
+    order[pos] = c;
   }
 }
 

@@ -82,7 +82,8 @@ Layout make_layout(const ssd_problem &p) {
   L.nc_max = p.num_seqs > 0 ? p.seqlen / Q + p.num_seqs
                             : (int64_t)p.batch * ((p.seqlen + Q - 1) / Q);
   L.rec_off = p.num_seqs > 0 ? (int64_t)round_up(3 + (size_t)p.num_seqs, 4) : 0;
-  const size_t plan_ints = p.num_seqs > 0 ? (size_t)(L.rec_off + 4 * L.nc_max) : 4;
+  // varlen: header, first chunk per sequence, 4-int records, chunk order
+  const size_t plan_ints = p.num_seqs > 0 ? (size_t)(L.rec_off + 5 * L.nc_max) : 4;
   L.path = path_of(p);
   L.mfma = L.path != kGeneric;
   const bool unfused = L.path == kGeneric || L.path == kMfmaUnfused;  // per-chunk intermediates
@@ -180,6 +181,7 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.nc_max = (int32_t)L.nc_max;
   a.heads_per_group = p->nheads / p->ngroups;
   a.rec_off = (int32_t)L.rec_off;
+  a.order_off = (int32_t)(L.rec_off + 4 * L.nc_max);
   return a;
 }
 
@@ -326,7 +328,7 @@ ssd_status ssd_validate(const ssd_problem *p) {
   const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->batch;
   const int64_t sp_blocks = (int64_t)((p->headdim * p->dstate / 4 + 255) / 256) * p->nheads * nseq;
   const Layout L = make_layout(*p);
-  if (sp_blocks > INT32_MAX || L.nc_max * 4 + L.rec_off > INT32_MAX ||
+  if (sp_blocks > INT32_MAX || L.nc_max * 5 + L.rec_off > INT32_MAX ||
       L.nc_max * p->nheads > INT32_MAX)
     return fail(SSD_ERR_UNSUPPORTED, "problem too large for 32-bit grid indexing");
   return SSD_OK;

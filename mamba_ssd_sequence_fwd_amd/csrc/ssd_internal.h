@@ -38,6 +38,7 @@ struct Args {
   int32_t nc_max;       // chunk slots in the workspace
   int32_t heads_per_group;
   int32_t rec_off;      // int offset of the chunk records inside plan
+  int32_t order_off;    // int offset of the chunk order (by index in sequence) inside plan
 };
 
 // Ints ahead of the per-(sequence, head) counters in Args::sync.
