@@ -79,6 +79,46 @@ def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
     return cost
 
 
+# HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE
+# and WRITE_SIZE passes and recorded in profiles/ with the hash of the kernel
+# sources they were taken on. Reported only while the sources still match.
+TRAFFIC_PROFILES = {
+    ("ssd_chain", "2.7b-bf16"): ("ssd_chain_2.7b-bf16_hbm_bytes.md",
+                                 ("k_chain.hip", "mfma_common.h", "ssd_internal.h")),
+}
+
+
+def kernel_sources_sha256(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mamba_ssd_sequence_fwd_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter profile, or None."""
+    entry = TRAFFIC_PROFILES.get((kernel, workload))
+    if entry is None:
+        return None
+    path = os.path.join(ROOT, "profiles", entry[0])
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256(entry[1]):
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp: dict, w: si.Workload, budget_s: float) -> dict:
     """Time the fp64 oracle (as it stands) on this host over a bounded sample
     of (sequence, head) pairs of the same workload; scale to tokens/s."""
@@ -193,7 +233,8 @@ def main():
     # Every kernel of this path is HBM-bound by its algorithmic intensity
     # (flops/byte far below the bf16 ridge of ~312), so the roof is HBM.
     roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, w.name),
                 "mfma_frac": round(kd["TFLOP/s"] / (MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16"
                                                     else MFMA_FP32_PEAK_TFLOPS), 4)}
     path = cost["_path"]

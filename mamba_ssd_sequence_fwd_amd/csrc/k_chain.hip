@@ -242,6 +242,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   bf16x8 acA[N / 32], acB[N / 32];
   load_c_rows<N>(acA, cc + (size_t)min(32 * iA + 16 * uA + lr, k.len - 1) * ldb + 8 * lg);
   if (NH == 2) load_c_rows<N>(acB, cc + (size_t)min(32 * iB + 16 + lr, k.len - 1) * ldb + 8 * lg);
+  // Published count of the predecessor, read early: usually it is already
+  // there and step 4 need not poll.
+  const int pair = k.seq * a.H + h;
+  const bool first = k.idx == 0;
+  int early = 0;
+  if (!first && tid == 0)
+    early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   float dtv = 0.f;
   {
     const int t = min(tid, k.len - 1);
@@ -329,12 +336,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
 
   // ---- 4. h_in from the chain; h_out = 2^(cs_last) h_in + S_c ----------------------
-  const int pair = k.seq * a.H + h;
-  const bool first = k.idx == 0;
   int cs0, cs1;
   chunks_of_seq(a, k.seq, cs0, cs1);
   const bool last = c + 1 >= cs1;
-  if (!first && tid == 0 && !wait_published(pub + pair, k.idx))
+  if (!first && tid == 0 && early < k.idx && !wait_published(pub + pair, k.idx))
     __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();  // h_in published; every wave done reading the B slice
 
@@ -345,30 +350,37 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const float *h0 = a.h0 ? a.h0 + ((size_t)k.seq * a.H + h) * PN : nullptr;
   const float dec = exp2_fast(cs_last);
   bf16 *sH = sBH;
+  // ring slot layout: [wave][tile][r][lane], 256 contiguous bytes per
+  // access; every load is issued before the first store.
+  f32x4 hin[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int n = 16 * nt + 4 * lg, p = 16 * (pt0 + t) + lr;
-    // ring slot layout: [wave][tile][r][lane], 256 contiguous bytes per access
-    const size_t ro = ((size_t)(wave * TPW + t) * 4) * 64 + lane;
-    f32x4 hin = f32x4{0.f, 0.f, 0.f, 0.f};
+    hin[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (!first) {
+      const float *src = rin + (size_t)(wave * TPW + t) * 256 + lane;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hin[r] = ring_load(rin + ro + 64 * r);
+      for (int r = 0; r < 4; ++r) hin[t][r] = ring_load(src + 64 * r);
     } else if (h0) {
       const float4 v = *reinterpret_cast<const float4 *>(h0 + (size_t)p * N + n);
-      hin = f32x4{v.x, v.y, v.z, v.w};
+      hin[t] = f32x4{v.x, v.y, v.z, v.w};
     }
-    const f32x4 hout = dec * hin + hs[t];
-    if (!last) {
+  }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ring_store(rout + ro + 64 * r, hout[r]);
+  for (int t = 0; t < TPW; ++t) {
+    const int n = 16 * nt + 4 * lg, p = 16 * (pt0 + t) + lr;
+    const f32x4 hout = dec * hin[t] + hs[t];
+    if (!last) {
+      float *dst = rout + (size_t)(wave * TPW + t) * 256 + lane;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ring_store(dst + 64 * r, hout[r]);
     } else if (a.hT) {
       *reinterpret_cast<float4 *>(a.hT + ((size_t)k.seq * a.H + h) * PN + (size_t)p * N + n) =
           make_float4(hout[0], hout[1], hout[2], hout[3]);
     }
     uint2 hb;
-    hb.x = pack2(hin[0], hin[1]);
-    hb.y = pack2(hin[2], hin[3]);
+    hb.x = pack2(hin[t][0], hin[t][1]);
+    hb.y = pack2(hin[t][2], hin[t][3]);
     *reinterpret_cast<uint2 *>(sH + swz<N>(p, n)) = hb;
   }
   wait_vmem_all();  // this wave's ring stores have completed (device-coherent)
