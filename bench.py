@@ -120,8 +120,10 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(inp: dict, w: si.Workload, budget_s: float) -> dict:
-    """Time the fp64 oracle (as it stands) on this host over a bounded sample
-    of (sequence, head) pairs of the same workload; scale to tokens/s."""
+    """Time the fp64 oracle (as it stands) on this host over the same workload:
+    (sequence, head) pairs in a seeded random order, in batches, until the time
+    budget is spent (the whole workload, repeated if it takes less than the
+    budget); reported as tokens of the workload per second."""
     import oracle
     threads = oracle.default_threads()
     lens = inp["seq_lens"] or [w.seqlen] * w.batch
@@ -132,31 +134,25 @@ def cpu_baseline(inp: dict, w: si.Workload, budget_s: float) -> dict:
     C = inp["C"].reshape(-1, w.ngroups, w.dstate)
     all_pairs = [(s, h) for s in range(len(lens)) for h in range(H)]
     rng = np.random.default_rng(0)
-    order = rng.permutation(len(all_pairs))
-    # Probe with one pair per thread, then size the sample to the budget.
-    n = min(len(all_pairs), threads)
+    order = [all_pairs[i] for i in rng.permutation(len(all_pairs))]
     done, tok, elapsed = 0, 0, 0.0
-    while done < len(all_pairs):
-        batch = [all_pairs[i] for i in order[done:done + n]]
+    n = min(len(order), threads)  # first batch: one pair per thread
+    while elapsed < budget_s:
+        batch = [order[(done + i) % len(order)] for i in range(n)]
         t0 = time.perf_counter()
         oracle.ssd_pairs(x, dt, inp["A"], B, C, inp["D"], inp["h0"], lens, batch,
                          threads=threads)
         elapsed += time.perf_counter() - t0
         tok += sum(lens[s] for s, _ in batch)
         done += len(batch)
-        if elapsed > budget_s:
-            break
-        rate = elapsed / max(done, 1)
-        n = int(min(len(all_pairs) - done, max(threads, (budget_s - elapsed) / max(rate, 1e-9))))
-        if n <= 0:
-            break
-    # tokens of the whole workload per second: each pair is one head of one
-    # sequence; the job has H heads per token.
+        rate = elapsed / done
+        n = int(min(4 * len(order), max(threads, (budget_s - elapsed) / max(rate, 1e-9))))
+    # each pair is one head of one sequence; a token of the workload has H heads
     value = tok / H / elapsed
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d (sequence, head) pairs of the %s workload, %.1f s of "
-                      "fp64 recurrence over %d host threads" % (
-                          done, len(all_pairs), w.name, elapsed, threads)}
+            "sample": "%d (sequence, head) pairs of the %s workload (%d pairs, %.2f passes), "
+                      "%.1f s of fp64 recurrence over %d host threads" % (
+                          done, w.name, len(order), done / len(order), elapsed, threads)}
 
 
 def main():
@@ -170,7 +166,7 @@ def main():
                     help="run one kernel per step of the method instead of the fused kernel")
     ap.add_argument("--per-sequence", action="store_true",
                     help="run the fused kernel with one workgroup per (sequence, head)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy "
                          "of this many MiB (known HBM traffic) to calibrate byte counters")
