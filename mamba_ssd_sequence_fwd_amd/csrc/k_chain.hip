@@ -10,30 +10,36 @@
 // recurrence h_out = 2^(cs_last) h_in + S_c links the chunks of one
 // (sequence, head), and it is handed from the workgroup of chunk j to that
 // of chunk j+1 through a two-slot fp32 ring in device memory plus a
-// published-chunk counter. Per workgroup, with cs the log2-decay prefix of
-// dt*A inside the chunk:
+// published-chunk counter. Per workgroup (four waves), with cs the log2-decay
+// prefix of dt*A inside the chunk:
 //
-//   1. ticket -> (chunk, head); dt, the decay tables (cs, w, u) by a
-//      wavefront prefix; x and B of the chunk into LDS (direct global->LDS).
+//   1. ticket -> (chunk, head); x of the chunk into LDS (direct global->LDS),
+//      dt, the chunk's B^T operand tiles into registers; the decay tables
+//      (cs, w, u) by a wavefront prefix.
 //   2. S_c = (w o B)^T x (w_s = 2^(cs_last - cs_s) dt_s): the chunk's own
 //      state from a zero start (the chunk_state step).
-//   3. intra-chunk outputs: (C B^T o decay mask) (dt o x) + D x, with C B^T
-//      tiles precomputed once per (chunk, group).
-//   4. h_in from the previous chunk's workgroup (or the initial state / zero
-//      at a sequence start); h_out = 2^(cs_last) h_in + S_c goes to the ring
-//      (or to the final state after the sequence's last chunk) and is
-//      published (the state_passing step).
-//   5. outputs += 2^(cs_l) C_l h_in^T (the rest of the chunk_scan step); y.
+//   3. h_in from the previous chunk's workgroup (loaded while step 2 runs when
+//      it is already published), or the initial state / zero at a sequence
+//      start; h_out = 2^(cs_last) h_in + S_c goes to the ring (or to the final
+//      state after the sequence's last chunk) and is published (the
+//      state_passing step).
+//   4. outputs, per 32-row tile: (C B^T o decay mask)(dt o x) + D x with the
+//      C B^T tiles precomputed once per (chunk, group), plus 2^(cs_l) C_l h_in^T
+//      (the chunk_scan step); y.
 //
-// Steps 2-3 need nothing from other workgroups. Tickets from an atomic
-// counter order the work units by chunk index inside the sequence, then
-// sequence, then head, so the predecessor of a unit took its ticket a whole
-// chunk-index level earlier and has normally published by the time step 4
-// asks. A workgroup only ever waits on a smaller ticket, i.e. on one that is
-// already running, so the chain cannot deadlock whatever order the hardware
-// dispatches in. Every wait is bounded by a wall-clock limit; a wait that
-// runs out sets an error word instead of hanging (the outputs are then
-// wrong).
+// Tickets from an atomic counter order the work units by chunk index inside
+// the sequence, then sequence, then head, so the predecessor of a unit took
+// its ticket a whole chunk-index level earlier and has normally published by
+// the time step 3 asks. A workgroup only ever waits on a smaller ticket, i.e.
+// on one that is already running, so the chain cannot deadlock whatever order
+// the hardware dispatches in. Every wait is bounded by a wall-clock limit; a
+// wait that runs out sets an error word instead of hanging (the outputs are
+// then wrong).
+//
+// LDS holds only x (the operand both products read transposed) and h_in
+// (bf16), 52 KB at chunk 256, so three workgroups share a CU. Each wave owns
+// whole 32-row output tiles, so the two 16-row halves of a tile share every
+// x and h_in read.
 //
 // HBM traffic: x, y once; B, C, dt and the C B^T tiles once per head
 // through L2; 32 KB of fp32 state written and read per (chunk, head).
@@ -42,116 +48,152 @@
 namespace ssd {
 
 constexpr float kLog2eChain = 1.4426950408889634f;
+constexpr int kChainWaves = 4;
 
-// Intra-chunk outputs of the 16-row half tile (i, u), rows 32i+16u .. +15,
-// added into Y (transposed: lane holds column l = 32i + 16u + lane%16 and
-// rows p = 16pt + 4(lane/16) + r). Off-diagonal 32-token tiles j < i use the
-// split decay 2^(cs_l - cs_r0) 2^(cs_r0 - cs_e) 2^(cs_e - cs_s) (three
-// factors <= 1, e = last token of tile j, r0 = first row of tile i, the last
-// one folded into sU); the diagonal tile takes the exact masked exponent and
-// carries D on its diagonal. C B^T tiles stream from L2 two ahead.
+// Intra-chunk outputs of the 32-row tile i (rows 32i .. 32i+31), both 16-row
+// halves u, added into Y[u] (transposed: lane holds column l = 32i + 16u +
+// lane%16 and rows p = 16pt + 4(lane/16) + r). Off-diagonal 32-token tiles
+// j < i use the split decay 2^(cs_l - cs_r0) 2^(cs_r0 - cs_e) 2^(cs_e - cs_s)
+// (three factors <= 1, e = last token of tile j, r0 = first row of tile i,
+// the last one folded into sU); the diagonal tile takes the exact masked
+// exponent and carries D on its diagonal. C B^T tiles stream from L2 two
+// ahead; each x operand read serves both halves.
 template <int Q>
-__device__ __forceinline__ void intra_half(int i, int u, f32x4 (&Y)[4], const bf16 *sX,
+__device__ __forceinline__ void intra_tile(int i, f32x4 (&Y)[2][4], const bf16 *sX,
                                            const float *sCs, const float *sDt, const float *sU,
-                                           const bf16 *cbase, float dsk) {
-  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+                                           const bf16 *cbase, float dsk, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
   const int pair0 = i * (i + 1) / 2;
-  const int lloc = 16 * u + lr;
-  const float cs_l = sCs[32 * i + lloc];
   const float cs_r0 = sCs[32 * i];
-  const float rdec = exp2_fast(cs_l - cs_r0);
-
+  float cs_l[2], rdec[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    cs_l[u] = sCs[32 * i + 16 * u + lr];
+    rdec[u] = exp2_fast(cs_l[u] - cs_r0);
+  }
   const int xrow = 4 * lg + (lr >> 2);
   int xoff[4];
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) xoff[pt] = xrow * kP + tr_lane_off<kP>(16 * pt, xrow & 7);
 
-  bf16x8 m0 = ldg8(cbase + (size_t)(pair0 * 2 + u) * 512);
-  bf16x8 m1 = ldg8(cbase + (size_t)((pair0 + min(1, i)) * 2 + u) * 512);
+  bf16x8 m0[2], m1[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    m0[u] = ldg8(cbase + (size_t)(pair0 * 2 + u) * 512);
+    m1[u] = ldg8(cbase + (size_t)((pair0 + min(1, i)) * 2 + u) * 512);
+  }
 #pragma unroll 1
   for (int j = 0; j < i; ++j) {
-    bf16x8 m = m0;
-    m0 = m1;
-    m1 = ldg8(cbase + (size_t)((pair0 + min(j + 2, i)) * 2 + u) * 512);
-    const float fa = rdec * exp2_fast(cs_r0 - sCs[32 * j + 31]);
+    bf16x8 m[2] = {m0[0], m0[1]};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      m0[u] = m1[u];
+      m1[u] = ldg8(cbase + (size_t)((pair0 + min(j + 2, i)) * 2 + u) * 512);
+    }
+    const float e_r0 = exp2_fast(cs_r0 - sCs[32 * j + 31]);
     const float4 ua = *reinterpret_cast<const float4 *>(sU + 32 * j + 4 * lg);
     const float4 ub = *reinterpret_cast<const float4 *>(sU + 32 * j + 16 + 4 * lg);
     const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = (bf16)((float)m[e] * (fa * uu[e]));
+    for (int u = 0; u < 2; ++u) {
+      const float fa = rdec[u] * e_r0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[u][e] = (bf16)((float)m[u][e] * (fa * uu[e]));
+    }
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       const bf16x4 lo = ds_tr4(sX, 32 * j * kP + xoff[pt]);
       const bf16x4 hi = ds_tr4(sX, (32 * j + 16) * kP + xoff[pt]);
-      Y[pt] = mfma(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, m, Y[pt]);
+      const bf16x8 xv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(xv, m[u], Y[u][pt]);
     }
   }
   // Diagonal tile j = i (m0 holds it: the stream clamps at i).
   {
-    bf16x8 m = m0;
     const float4 ca = *reinterpret_cast<const float4 *>(sCs + 32 * i + 4 * lg);
     const float4 cb4 = *reinterpret_cast<const float4 *>(sCs + 32 * i + 16 + 4 * lg);
     const float4 da = *reinterpret_cast<const float4 *>(sDt + 32 * i + 4 * lg);
     const float4 db = *reinterpret_cast<const float4 *>(sDt + 32 * i + 16 + 4 * lg);
     const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb4.x, cb4.y, cb4.z, cb4.w};
     const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+    bf16x8 m[2] = {m0[0], m0[1]};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sloc = 16 * (e >> 2) + 4 * lg + (e & 3);
-      const float v = (float)m[e] * exp2_fast(cs_l - cc[e]) * dd[e];
-      const float w = sloc == lloc ? v + dsk : v;
-      m[e] = (bf16)(sloc <= lloc ? w : 0.f);
+    for (int u = 0; u < 2; ++u) {
+      const int lloc = 16 * u + lr;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sloc = 16 * (e >> 2) + 4 * lg + (e & 3);
+        const float v = (float)m[u][e] * exp2_fast(cs_l[u] - cc[e]) * dd[e];
+        const float w = sloc == lloc ? v + dsk : v;
+        m[u][e] = (bf16)(sloc <= lloc ? w : 0.f);
+      }
     }
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       const bf16x4 lo = ds_tr4(sX, 32 * i * kP + xoff[pt]);
       const bf16x4 hi = ds_tr4(sX, (32 * i + 16) * kP + xoff[pt]);
-      Y[pt] = mfma(bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, m, Y[pt]);
+      const bf16x8 xv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(xv, m[u], Y[u][pt]);
     }
   }
 }
 
-// State part of half tile (i, u): Y += 2^(cs_l) C_l h_in^T, then y (bf16).
-// sH = h_in bf16 [p][n] (swizzled rows of N); ac = C row l of this group
-// (load_c_rows of the row clamped into the chunk, offset by 8*(lane/16));
-// rows l >= len are neither used nor stored.
+// C rows of the 32-row tile i, both halves: row 32i + 16u + lane%16 (clamped
+// into the chunk), n = 32ks + 8(lane/16) .. +7.
 template <int N>
-__device__ __forceinline__ void load_c_rows(bf16x8 (&ac)[N / 32], const bf16 *crow) {
+__device__ __forceinline__ void load_c_tile(bf16x8 (&ac)[2][N / 32], const bf16 *cc, size_t ldb,
+                                            int i, int len, int lane) {
 #pragma unroll
-  for (int ks = 0; ks < N / 32; ++ks) ac[ks] = ldg8(crow + 32 * ks);
+  for (int u = 0; u < 2; ++u) {
+    const bf16 *row = cc + (size_t)min(32 * i + 16 * u + (lane & 15), len - 1) * ldb +
+                      8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks) ac[u][ks] = ldg8(row + 32 * ks);
+  }
 }
 
+// State part of tile i: Y[u] += 2^(cs_l) C_l h_in^T, then y (bf16) for the
+// rows l < len. sH = h_in bf16 [p][n] (swizzled rows of N); each h_in read
+// serves both halves.
 template <int N>
-__device__ __forceinline__ void state_half_store(int i, int u, f32x4 (&Y)[4], const bf16 *sH,
-                                                 const float *sCs, const bf16x8 (&ac)[N / 32],
-                                                 int len, bf16 *y, size_t ystride) {
-  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int l = 32 * i + 16 * u + lr;
-  const bool valid = l < len;
-  f32x4 S[4];
+__device__ __forceinline__ void state_tile_store(int i, f32x4 (&Y)[2][4], const bf16 *sH,
+                                                 const float *sCs, const bf16x8 (&ac)[2][N / 32],
+                                                 int len, bf16 *y, size_t ystride, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+  f32x4 S[2][4];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) S[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) S[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < N / 32; ++ks) {
-    const bf16x8 acv = valid ? ac[ks] : zero8();
+    bf16x8 acv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acv[u] = 32 * i + 16 * u + lr < len ? ac[u][ks] : zero8();
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       const bf16x8 bh =
           *reinterpret_cast<const bf16x8 *>(sH + swz<N>(16 * pt + lr, 32 * ks + 8 * lg));
-      S[pt] = mfma(bh, acv, S[pt]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) S[u][pt] = mfma(bh, acv[u], S[u][pt]);
     }
   }
-  const float f = exp2_fast(sCs[l]);
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) Y[pt] += f * S[pt];
-  if (valid) {
-    bf16 *yr = y + (size_t)l * ystride + 4 * lg;
+  for (int u = 0; u < 2; ++u) {
+    const int l = 32 * i + 16 * u + lr;
+    const float f = exp2_fast(sCs[l]);
+    if (l < len) {
+      bf16 *yr = y + (size_t)l * ystride + 4 * lg;
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      uint2 o;
-      o.x = pack2(Y[pt][0], Y[pt][1]);
-      o.y = pack2(Y[pt][2], Y[pt][3]);
-      *reinterpret_cast<uint2 *>(yr + 16 * pt) = o;
+      for (int pt = 0; pt < 4; ++pt) {
+        const f32x4 v = Y[u][pt] + f * S[u][pt];
+        uint2 o;
+        o.x = pack2(v[0], v[1]);
+        o.y = pack2(v[2], v[3]);
+        *reinterpret_cast<uint2 *>(yr + 16 * pt) = o;
+      }
     }
   }
 }
@@ -182,38 +224,69 @@ __device__ __forceinline__ bool wait_published(const int32_t *ctr, int want) {
   return true;
 }
 
+// Incoming state of head h, chunk k, in the state-tile layout of this wave
+// (tile (j, pt): rows n = 16 (nt0 + j) + 4(lane/16) + r, column p = 16 pt +
+// lane%16): the ring slot of the previous chunk, or at a sequence start the
+// initial state (or zeros). Ring slot layout: [wave][j][pt][r][lane], 256
+// contiguous bytes per access.
+template <int N, int NTW>
+__device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, const Chunk &k,
+                                          int h, int wave, int nt0, int lane) {
+  const size_t PN = (size_t)kP * N;
+  const int lr = lane & 15, lg = lane >> 4;
+  if (k.idx > 0) {
+    const float *rin =
+        a.ring + ((size_t)(k.seq * a.H + h) * 2 + ((k.idx + 1) & 1)) * PN + (size_t)wave * NTW * 4 * 256;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hin[j][pt][r] = ring_load(rin + ((j * 4 + pt) * 4 + r) * 64 + lane);
+  } else if (a.h0) {
+    const float *h0 = a.h0 + (size_t)(k.seq * a.H + h) * PN;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
+        const float4 v = *reinterpret_cast<const float4 *>(h0 + (size_t)p * N + n);
+        hin[j][pt] = f32x4{v.x, v.y, v.z, v.w};
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hin[j][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 template <int N, int Q>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_ssd_chain(
-    Args a, const bf16 *cb, const bf16 *zeros) {
-  constexpr int T = Q / 32, PAIRS = T * (T + 1) / 2;
-  constexpr int QB = Q * N <= 16384 ? Q : 16384 / N;  // tokens per B slice (32 KB of LDS)
-  constexpr int NSL = Q / QB;
-  constexpr int NT16 = N / 16;        // 16-row n tiles of the state
-  constexpr int TPW = N / 32;         // state tiles per wave (8 waves, 4 p tiles)
-  constexpr int SBH = QB * N > kP * N ? QB * N : kP * N;
+__global__ __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
+  constexpr int T = Q / 32, PAIRS = T * (T + 1) / 2, NKS = Q / 32;
+  constexpr int NTW = N / 64;                 // 16-row n tiles of the state per wave
+  constexpr int NTILE = T == 8 ? 2 : 1;       // 32-row output tiles per wave
   static_assert(Q == 128 || Q == 256, "chain kernel: chunk 128 or 256");
   static_assert(N == 64 || N == 128, "chain kernel: N 64 or 128");
-  static_assert(NSL <= 2, "at most two B slices");
   __shared__ __attribute__((aligned(16))) bf16 sX[Q * kP];  // x, [token][p]
-  __shared__ __attribute__((aligned(16))) bf16 sBH[SBH];    // B slice [token][n], then h_in [p][n]
+  __shared__ __attribute__((aligned(16))) bf16 sH[kP * N];  // h_in (bf16), [p][n]
   __shared__ __attribute__((aligned(16))) float sCs[Q];
   __shared__ __attribute__((aligned(16))) float sDt[Q];
   __shared__ __attribute__((aligned(16))) float sU[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];
   __shared__ float sTot[4];
-  __shared__ int sTicket;
+  __shared__ int sTicket, sReady;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   int32_t *ticket = a.sync, *err = a.sync + 1, *pub = a.sync + kSyncHeader;
 
-  // ---- 1. work unit, decay tables, x and B into LDS ---------------------------
+  // ---- 1. work unit, loads, decay tables -----------------------------------
   if (tid == 0) sTicket = atomicAdd(ticket, 1);
   __syncthreads();
   const int tk = sTicket;
-  // Ticket order: chunk index by chunk index across all sequences (all first
-  // chunks, then all second chunks, ...), so a chunk's predecessor is many
-  // tickets back and has usually finished by then.
   int c, h;
   if (!a.varlen) {
     const int per = a.nseq * a.H;
@@ -229,27 +302,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   Chunk k;
   if (!chunk_of(a, c, k)) return;
   const int g = h / a.heads_per_group;
-  const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N;
+  const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N, PN = (size_t)kP * N;
   const bf16 *xc = static_cast<const bf16 *>(a.x) + (size_t)k.start * ldx + (size_t)h * kP;
-  const bf16 *bc = static_cast<const bf16 *>(a.B) + (size_t)k.start * ldb + (size_t)g * N;
   const bf16 *cc = static_cast<const bf16 *>(a.C) + (size_t)k.start * ldb + (size_t)g * N;
-  async_tile<kP, Q>(sX, xc, ldx, k.len, zeros);
-  async_tile<N, QB>(sBH, bc, ldb, k.len, zeros);
-  // C rows of this wave's output half tiles (used last; loaded first).
-  constexpr int NH = T == 8 ? 2 : 1;  // half tiles per wave
-  const int iA = T == 8 ? wave : wave >> 1, uA = T == 8 ? 0 : wave & 1;
-  const int iB = T - 1 - wave;
-  bf16x8 acA[N / 32], acB[N / 32];
-  load_c_rows<N>(acA, cc + (size_t)min(32 * iA + 16 * uA + lr, k.len - 1) * ldb + 8 * lg);
-  if (NH == 2) load_c_rows<N>(acB, cc + (size_t)min(32 * iB + 16 + lr, k.len - 1) * ldb + 8 * lg);
-  // Published count of the predecessor, read early: usually it is already
-  // there and step 4 need not poll.
+  async_rows<kP, Q, kChainWaves>(sX, xc, ldx, k.len, lane);
+  const int nt0 = wave * NTW;
+  // This wave's B^T operand tiles (n tiles nt0.., every 32-token step).
+  const bf16 *btc = bt + (((size_t)c * a.G + g) * (N / 16) + nt0) * NKS * 512 + lane * 8;
+  bf16x8 bts[NTW][NKS];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) bts[j][ks] = ldg8(btc + (size_t)(j * NKS + ks) * 512);
   const int pair = k.seq * a.H + h;
   const bool first = k.idx == 0;
-  int early = 0;
+  int early = 0;  // published count of the predecessor, read early
   if (!first && tid == 0)
     early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float dtv = 0.f;
+  float dtv;
   {
     const int t = min(tid, k.len - 1);
     const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
@@ -259,6 +329,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const float dsk = a.D ? a.D[h] : 0.f;
   const float incl = wave_inclusive_sum(dtv * ah);
   if (lane == 63 && wave < Q / 64) sTot[wave] = incl;
+  if (tid == 0) sReady = (first || early >= k.idx) ? 1 : 0;
   __syncthreads();
   float pre = 0.f, cs_last = 0.f;
 #pragma unroll
@@ -267,6 +338,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     pre += w < wave ? t : 0.f;
     cs_last += t;
   }
+  const bool ready = sReady != 0;
   const float cst = incl + pre;
   const float cs_tile_end = __shfl(cst, lane | 31);
   if (tid < Q) {
@@ -275,123 +347,108 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     sW[tid] = exp2_fast(cs_last - cst) * dtv;
     sU[tid] = exp2_fast(cs_tile_end - cst) * dtv;
   }
-  wait_vmem_all();
+  wait_vmem_all();  // x has landed
   __syncthreads();
 
-  // ---- 2. S_c = (w o B)^T x, state tiles (n tile nt, p tile pt0 + q) -------------
-  const int nt = wave % NT16, pt0 = (wave / NT16) * TPW;
+  // ---- 2. S_c = (w o B)^T x; h_in loads in flight when already published ------
+  f32x4 hin[NTW][4];
+  if (ready) load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
+  f32x4 hs[NTW][4];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) hs[j][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int trow = 8 * lg + (lr >> 2);
-  int boff[2], xoff[TPW][2];
+  int xoff[4][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int r = trow + 4 * q;
-    boff[q] = r * N + tr_lane_off<N>(16 * nt, r & 7);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) xoff[t][q] = r * kP + tr_lane_off<kP>(16 * (pt0 + t), r & 7);
+    for (int pt = 0; pt < 4; ++pt) xoff[pt][q] = r * kP + tr_lane_off<kP>(16 * pt, r & 7);
   }
-  f32x4 hs[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) hs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto state_slice = [&](int sl) {
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int s0 = 32 * ks;
+    const float4 wa = *reinterpret_cast<const float4 *>(sW + s0 + 8 * lg);
+    const float4 wb = *reinterpret_cast<const float4 *>(sW + s0 + 8 * lg + 4);
+    const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    bf16x8 av[NTW];
 #pragma unroll
-    for (int ks = 0; ks < QB / 32; ++ks) {
-      const int s0 = sl * QB + 32 * ks;
-      const float4 wa = *reinterpret_cast<const float4 *>(sW + s0 + 8 * lg);
-      const float4 wb = *reinterpret_cast<const float4 *>(sW + s0 + 8 * lg + 4);
-      const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-      const bf16x4 lo = ds_tr4(sBH, 32 * ks * N + boff[0]);
-      const bf16x4 hi = ds_tr4(sBH, 32 * ks * N + boff[1]);
-      const bf16 raw[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      bf16x8 av;
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) av[e] = (bf16)((float)raw[e] * ww[e]);
+      for (int e = 0; e < 8; ++e) av[j][e] = (bf16)((float)bts[j][ks][e] * ww[e]);
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const bf16x4 xl = ds_tr4(sX, s0 * kP + xoff[t][0]);
-        const bf16x4 xh = ds_tr4(sX, s0 * kP + xoff[t][1]);
-        hs[t] = mfma(av, bf16x8{xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]}, hs[t]);
-      }
+    for (int pt = 0; pt < 4; ++pt) {
+      const bf16x4 xl = ds_tr4(sX, s0 * kP + xoff[pt][0]);
+      const bf16x4 xh = ds_tr4(sX, s0 * kP + xoff[pt][1]);
+      const bf16x8 xv = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) hs[j][pt] = mfma(av[j], xv, hs[j][pt]);
     }
-  };
-  state_slice(0);
-  if (NSL == 2) {
-    __syncthreads();  // every wave done with the first B slice
-    async_tile<N, QB>(sBH, bc + (size_t)QB * ldb, ldb, k.len - QB, zeros);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- 3. intra-chunk outputs (the second B slice lands meanwhile) -----------------
-  const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
-  f32x4 Y[NH][4];
-#pragma unroll
-  for (int t = 0; t < NH; ++t)
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) Y[t][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  intra_half<Q>(iA, uA, Y[0], sX, sCs, sDt, sU, cbase, dsk);
-  if (NH == 2) intra_half<Q>(iB, 1, Y[NH - 1], sX, sCs, sDt, sU, cbase, dsk);
-
-  if (NSL == 2) {
-    wait_vmem_all();
+  // ---- 3. h_in; h_out = 2^(cs_last) h_in + S_c to the ring; publish ------------
+  const int iA = T == 8 ? wave : wave, iB = T - 1 - wave;
+  bf16x8 acA[2][N / 32];
+  load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);  // used after the hand-off
+  if (!ready) {
+    if (tid == 0 && !wait_published(pub + pair, k.idx))
+      __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    state_slice(1);
+    load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
   }
-
-  // ---- 4. h_in from the chain; h_out = 2^(cs_last) h_in + S_c ----------------------
   int cs0, cs1;
   chunks_of_seq(a, k.seq, cs0, cs1);
   const bool last = c + 1 >= cs1;
-  if (!first && tid == 0 && early < k.idx && !wait_published(pub + pair, k.idx))
-    __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();  // h_in published; every wave done reading the B slice
-
-  const size_t PN = (size_t)kP * N;
-  float *ring = a.ring + (size_t)pair * 2 * PN;
-  const float *rin = ring + (size_t)((k.idx + 1) & 1) * PN;  // slot of chunk idx-1
-  float *rout = ring + (size_t)(k.idx & 1) * PN;
-  const float *h0 = a.h0 ? a.h0 + ((size_t)k.seq * a.H + h) * PN : nullptr;
   const float dec = exp2_fast(cs_last);
-  bf16 *sH = sBH;
-  // ring slot layout: [wave][tile][r][lane], 256 contiguous bytes per
-  // access; every load is issued before the first store.
-  f32x4 hin[TPW];
+  float *rout = a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN + (size_t)wave * NTW * 4 * 256;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int n = 16 * nt + 4 * lg, p = 16 * (pt0 + t) + lr;
-    hin[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (!first) {
-      const float *src = rin + (size_t)(wave * TPW + t) * 256 + lane;
+  for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hin[t][r] = ring_load(src + 64 * r);
-    } else if (h0) {
-      const float4 v = *reinterpret_cast<const float4 *>(h0 + (size_t)p * N + n);
-      hin[t] = f32x4{v.x, v.y, v.z, v.w};
+    for (int pt = 0; pt < 4; ++pt) {
+      const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
+      const f32x4 hout = dec * hin[j][pt] + hs[j][pt];
+      if (!last) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ring_store(rout + ((j * 4 + pt) * 4 + r) * 64 + lane, hout[r]);
+      } else if (a.hT) {
+        *reinterpret_cast<float4 *>(a.hT + (size_t)pair * PN + (size_t)p * N + n) =
+            make_float4(hout[0], hout[1], hout[2], hout[3]);
+      }
+      uint2 hb;
+      hb.x = pack2(hin[j][pt][0], hin[j][pt][1]);
+      hb.y = pack2(hin[j][pt][2], hin[j][pt][3]);
+      *reinterpret_cast<uint2 *>(sH + swz<N>(p, n)) = hb;
     }
-  }
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int n = 16 * nt + 4 * lg, p = 16 * (pt0 + t) + lr;
-    const f32x4 hout = dec * hin[t] + hs[t];
-    if (!last) {
-      float *dst = rout + (size_t)(wave * TPW + t) * 256 + lane;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ring_store(dst + 64 * r, hout[r]);
-    } else if (a.hT) {
-      *reinterpret_cast<float4 *>(a.hT + ((size_t)k.seq * a.H + h) * PN + (size_t)p * N + n) =
-          make_float4(hout[0], hout[1], hout[2], hout[3]);
-    }
-    uint2 hb;
-    hb.x = pack2(hin[t][0], hin[t][1]);
-    hb.y = pack2(hin[t][2], hin[t][3]);
-    *reinterpret_cast<uint2 *>(sH + swz<N>(p, n)) = hb;
-  }
   wait_vmem_all();  // this wave's ring stores have completed (device-coherent)
   __syncthreads();  // ... and every other wave's; sH complete
   if (!last && tid == 0)
     __hip_atomic_store(pub + pair, k.idx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // ---- 5. outputs += 2^(cs_l) C_l h_in^T; y ------------------------------------------
+  // ---- 4. outputs, one 32-row tile at a time ------------------------------------
+  const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   bf16 *yc = static_cast<bf16 *>(a.y) + (size_t)k.start * ldx + (size_t)h * kP;
-  state_half_store<N>(iA, uA, Y[0], sH, sCs, acA, k.len, yc, ldx);
-  if (NH == 2) state_half_store<N>(iB, 1, Y[NH - 1], sH, sCs, acB, k.len, yc, ldx);
+  {
+    f32x4 Y[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    intra_tile<Q>(iA, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
+    state_tile_store<N>(iA, Y, sH, sCs, acA, k.len, yc, ldx, lane);
+  }
+  if (NTILE == 2) {
+    bf16x8 acB[2][N / 32];
+    load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);
+    f32x4 Y[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    intra_tile<Q>(iB, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
+    state_tile_store<N>(iB, Y, sH, sCs, acB, k.len, yc, ldx, lane);
+  }
 }
 
 // Final state of every (sequence, head) whose sequence has no tokens (no
@@ -419,21 +476,21 @@ bool chain_path_supports(const Args &a) {
 }
 
 template <int N, int Q>
-static hipError_t launch_chain_nq(const Args &a, const void *cb, const void *zeros,
+static hipError_t launch_chain_nq(const Args &a, const void *cb, const void *bt,
                                   hipStream_t st) {
   const int64_t blocks = (int64_t)a.nc_max * a.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_ssd_chain<N, Q>), dim3((unsigned)blocks), dim3(512), 0, st, a,
-                     static_cast<const bf16 *>(cb), static_cast<const bf16 *>(zeros));
+  hipLaunchKernelGGL((k_ssd_chain<N, Q>), dim3((unsigned)blocks), dim3(64 * kChainWaves), 0, st,
+                     a, static_cast<const bf16 *>(cb), static_cast<const bf16 *>(bt));
   return hipGetLastError();
 }
 
-hipError_t launch_chain(const Args &a, const void *cb, const void *zeros, hipStream_t st) {
+hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream_t st) {
   if (a.N == 64)
-    return a.Q == 128 ? launch_chain_nq<64, 128>(a, cb, zeros, st)
-                      : launch_chain_nq<64, 256>(a, cb, zeros, st);
-  return a.Q == 128 ? launch_chain_nq<128, 128>(a, cb, zeros, st)
-                    : launch_chain_nq<128, 256>(a, cb, zeros, st);
+    return a.Q == 128 ? launch_chain_nq<64, 128>(a, cb, bt, st)
+                      : launch_chain_nq<64, 256>(a, cb, bt, st);
+  return a.Q == 128 ? launch_chain_nq<128, 128>(a, cb, bt, st)
+                    : launch_chain_nq<128, 256>(a, cb, bt, st);
 }
 
 }  // namespace ssd

@@ -180,6 +180,27 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
       }
     }
   }
+  // Chain path: B^T of this chunk and group in the A-operand layout of the
+  // chunk-state product (tile (nt, ks), lane L: n = 16 nt + L%16, tokens
+  // 32 ks + 8 (L/16) .. +7, zeros past the chunk end); this block does the
+  // two 32-token steps 2w and 2w+1, transposing through LDS.
+  if (a.bt) {
+    __shared__ __attribute__((aligned(16))) bf16 sBt[32 * N];
+    bf16 *btb = static_cast<bf16 *>(a.bt) + ((size_t)c * a.G + g) * (N / 16) * (Q / 32) * 512;
+#pragma unroll 1
+    for (int q = 0; q < 2; ++q) {
+      const int ks = 2 * w + q;
+      RowStager<N, 32, 64> st;
+      st.load(B, ldr, 32 * ks, k.len);
+      __syncthreads();  // the previous step's transposed reads are done
+      st.store(sBt);
+      __syncthreads();
+#pragma unroll
+      for (int nt = 0; nt < N / 16; ++nt)
+        *reinterpret_cast<bf16x8 *>(btb + ((size_t)nt * (Q / 32) + ks) * 512 + lane * 8) =
+            tr_operand<N>(sBt, 0, 16 * nt);
+    }
+  }
 }
 
 // ============================================================================

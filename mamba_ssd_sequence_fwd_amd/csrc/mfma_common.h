@@ -465,22 +465,22 @@ __device__ __forceinline__ void async_tile(bf16 *tile, const bf16 *src, size_t l
 }
 
 // Same copy with rows >= len read from row len - 1 instead (finite data the
-// caller multiplies by zero), so every lane addresses `src` (a workgroup-
-// uniform base) plus a 32-bit byte offset: no per-lane 64-bit addresses to
-// keep alive between copies. Needs len >= 1 and ROWS * ld * 2 < 2^31.
-// `lane` is the caller's lane index (pass an opaque copy inside loops).
-template <int W, int ROWS>
+// caller multiplies by zero), by a workgroup of NW waves. Every lane
+// addresses `src` (a workgroup-uniform base) plus a 32-bit byte offset, so no
+// per-lane 64-bit addresses stay alive between copies. Needs len >= 1 and
+// ROWS * ld * 2 < 2^31.
+template <int W, int ROWS, int NW>
 __device__ __forceinline__ void async_rows(bf16 *tile, const bf16 *src, size_t ld, int len,
                                            int lane) {
-  constexpr int R = 512 / W;
-  constexpr int NI = ROWS / R;
-  static_assert(NI % 8 == 0, "tile must split over 8 waves");
+  constexpr int R = 512 / W;   // rows per 1 KB wave instruction
+  constexpr int NI = ROWS / R; // wave instructions for the tile
+  static_assert(NI % NW == 0, "tile must split evenly over the waves");
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane / (W / 8), pc = lane % (W / 8);
   const char *base = reinterpret_cast<const char *>(src);
 #pragma unroll
-  for (int k = 0; k < NI / 8; ++k) {
-    const int m = wave + 8 * k;
+  for (int k = 0; k < NI / NW; ++k) {
+    const int m = wave + NW * k;
     const int s = m * R + rl;
     const int c = (pc & ~7) | ((pc & 7) ^ (s & 7));
     const uint32_t off = (uint32_t)min(s, len - 1) * (uint32_t)(ld * 2) + 16u * (uint32_t)c;

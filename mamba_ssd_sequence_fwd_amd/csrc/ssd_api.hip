@@ -57,7 +57,7 @@ enum Path {
 struct Layout {
   int64_t nc_max;
   int64_t rec_off;  // int32 offset of the chunk records in the plan area
-  size_t plan, cs, states, cb, zeros, sync, ring, total;
+  size_t plan, cs, states, cb, bt, zeros, sync, ring, total;
   int64_t nsync;
   Path path;
   bool mfma;
@@ -101,6 +101,9 @@ Layout make_layout(const ssd_problem &p) {
     const int64_t T = Q / 32;
     off = round_up(off + (size_t)L.nc_max * p.ngroups * (T * (T + 1) / 2) * 2 * 1024, kAlign);
   }
+  L.bt = off;  // chain path: B^T operand tiles, (chunks, G, N/16, Q/32) x 1 KB
+  if (L.path == kMfmaChain)
+    off = round_up(off + (size_t)L.nc_max * p.ngroups * (p.dstate / 16) * (Q / 32) * 1024, kAlign);
   L.zeros = off;
   if (L.mfma) off += kAlign;
   const int64_t nseq = p.num_seqs > 0 ? p.num_seqs : p.batch;
@@ -165,6 +168,7 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.states = reinterpret_cast<float *>(ws + L.states);
   a.cb = ws + L.cb;
   a.zeros = ws + L.zeros;
+  a.bt = L.path == kMfmaChain ? ws + L.bt : nullptr;
   a.sync = reinterpret_cast<int32_t *>(ws + L.sync);
   a.ring = reinterpret_cast<float *>(ws + L.ring);
   a.nsync = (int32_t)L.nsync;
@@ -250,7 +254,7 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
   if (L.path == kMfmaChain) {
     if (a.nc_max > 0) {
       SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
-      SSD_LAUNCH(ssd::launch_chain(a, a.cb, a.zeros, s), "ssd_chain");
+      SSD_LAUNCH(ssd::launch_chain(a, a.cb, a.bt, s), "ssd_chain");
     }
     if (chain_needs_empty_pass(a))
       SSD_LAUNCH(ssd::launch_final_of_empty(a, s), "final_of_empty");

@@ -27,6 +27,7 @@ struct Args {
   float *states;        // (chunks, H, P, N)
   void *cb;             // bf16 C B^T tiles (MFMA path only)
   void *zeros;          // 256 zero bytes (written by the C B^T kernel)
+  void *bt;             // chain path: bf16 B^T operand tiles per (chunk, group), or null
   int32_t *sync;        // chain path: [0] ticket, [1] error word, [kSyncHeader + seq*H + h]
                         // published-chunk counters; zeroed by the C B^T kernel
   float *ring;          // chain path: (S, H, 2, P, N) fp32 state hand-off ring
@@ -159,7 +160,7 @@ hipError_t launch_chunk_scan_mfma(const Args &a, const void *cb, hipStream_t s);
 bool fused_path_supports(const Args &a);
 hipError_t launch_fused(const Args &a, const void *cb, const void *zeros, hipStream_t s);
 bool chain_path_supports(const Args &a);
-hipError_t launch_chain(const Args &a, const void *cb, const void *zeros, hipStream_t s);
+hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream_t s);
 hipError_t launch_final_of_empty(const Args &a, hipStream_t s);
 
 }  // namespace ssd
