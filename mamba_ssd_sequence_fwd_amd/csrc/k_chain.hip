@@ -154,19 +154,20 @@ __device__ __forceinline__ void load_c_tile(bf16x8 (&ac)[2][N / 32], const bf16 
   }
 }
 
-// State part of tile i: Y[u] += 2^(cs_l) C_l h_in^T, then y (bf16) for the
-// rows l < len. sH = h_in bf16 [p][n] (swizzled rows of N); each h_in read
-// serves both halves.
+// State part of tile i, computed first: Y[u] = 2^(cs_l) C_l h_in^T (the
+// intra-chunk part then accumulates on top). sH = h_in bf16 [p][n] (swizzled
+// rows of N); each h_in read serves both halves; C rows past len are zero.
 template <int N>
-__device__ __forceinline__ void state_tile_store(int i, f32x4 (&Y)[2][4], const bf16 *sH,
-                                                 const float *sCs, const bf16x8 (&ac)[2][N / 32],
-                                                 int len, bf16 *y, size_t ystride, int lane) {
+__device__ __forceinline__ void state_tile(int i, f32x4 (&Y)[2][4], const bf16 *sH,
+                                           const float *sCs, const bf16x8 (&ac)[2][N / 32],
+                                           int len, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  f32x4 S[2][4];
+  int hbase = 0;
+  asm volatile("" : "+v"(hbase));
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) S[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < N / 32; ++ks) {
     bf16x8 acv[2];
@@ -174,24 +175,32 @@ __device__ __forceinline__ void state_tile_store(int i, f32x4 (&Y)[2][4], const 
     for (int u = 0; u < 2; ++u) acv[u] = 32 * i + 16 * u + lr < len ? ac[u][ks] : zero8();
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-      const bf16x8 bh =
-          *reinterpret_cast<const bf16x8 *>(sH + swz<N>(16 * pt + lr, 32 * ks + 8 * lg));
+      const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(
+          sH + hbase + swz<N>(16 * pt + lr, 32 * ks + 8 * lg));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) S[u][pt] = mfma(bh, acv[u], S[u][pt]);
+      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(bh, acv[u], Y[u][pt]);
     }
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int l = 32 * i + 16 * u + lr;
-    const float f = exp2_fast(sCs[l]);
+    const float f = exp2_fast(sCs[32 * i + 16 * u + lr]);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) Y[u][pt] *= f;
+  }
+}
+
+__device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int len, bf16 *y,
+                                           size_t ystride, int lane) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int l = 32 * i + 16 * u + (lane & 15);
     if (l < len) {
-      bf16 *yr = y + (size_t)l * ystride + 4 * lg;
+      bf16 *yr = y + (size_t)l * ystride + 4 * (lane >> 4);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const f32x4 v = Y[u][pt] + f * S[u][pt];
         uint2 o;
-        o.x = pack2(v[0], v[1]);
-        o.y = pack2(v[2], v[3]);
+        o.x = pack2(Y[u][pt][0], Y[u][pt][1]);
+        o.y = pack2(Y[u][pt][2], Y[u][pt][3]);
         *reinterpret_cast<uint2 *>(yr + 16 * pt) = o;
       }
     }
@@ -307,13 +316,15 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   const bf16 *cc = static_cast<const bf16 *>(a.C) + (size_t)k.start * ldb + (size_t)g * N;
   async_rows<kP, Q, kChainWaves>(sX, xc, ldx, k.len, lane);
   const int nt0 = wave * NTW;
-  // This wave's B^T operand tiles (n tiles nt0.., every 32-token step).
+  // This wave's B^T operand tiles (n tiles nt0..), streamed KPF 32-token
+  // steps ahead of their use; the first KPF steps now.
+  constexpr int KPF = NKS < 4 ? NKS : 4;
   const bf16 *btc = bt + (((size_t)c * a.G + g) * (N / 16) + nt0) * NKS * 512 + lane * 8;
-  bf16x8 bts[NTW][NKS];
+  bf16x8 bts[NTW][KPF];
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) bts[j][ks] = ldg8(btc + (size_t)(j * NKS + ks) * 512);
+    for (int ks = 0; ks < KPF; ++ks) bts[j][ks] = ldg8(btc + (size_t)(j * NKS + ks) * 512);
   const int pair = k.seq * a.H + h;
   const bool first = k.idx == 0;
   int early = 0;  // published count of the predecessor, read early
@@ -374,9 +385,11 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
     bf16x8 av[NTW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int j = 0; j < NTW; ++j) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) av[j][e] = (bf16)((float)bts[j][ks][e] * ww[e]);
+      for (int e = 0; e < 8; ++e) av[j][e] = (bf16)((float)bts[j][ks % KPF][e] * ww[e]);
+      if (ks + KPF < NKS) bts[j][ks % KPF] = ldg8(btc + (size_t)(j * NKS + ks + KPF) * 512);
+    }
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       const bf16x4 xl = ds_tr4(sX, s0 * kP + xoff[pt][0]);
@@ -429,25 +442,19 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   // ---- 4. outputs, one 32-row tile at a time ------------------------------------
   const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   bf16 *yc = static_cast<bf16 *>(a.y) + (size_t)k.start * ldx + (size_t)h * kP;
+  bf16x8 acB[2][N / 32];
+  if (NTILE == 2) load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);  // in flight during tile A
   {
     f32x4 Y[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    state_tile<N>(iA, Y, sH, sCs, acA, k.len, lane);
     intra_tile<Q>(iA, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
-    state_tile_store<N>(iA, Y, sH, sCs, acA, k.len, yc, ldx, lane);
+    store_tile(iA, Y, k.len, yc, ldx, lane);
   }
   if (NTILE == 2) {
-    bf16x8 acB[2][N / 32];
-    load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);
     f32x4 Y[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    state_tile<N>(iB, Y, sH, sCs, acB, k.len, lane);
     intra_tile<Q>(iB, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
-    state_tile_store<N>(iB, Y, sH, sCs, acB, k.len, yc, ldx, lane);
+    store_tile(iB, Y, k.len, yc, ldx, lane);
   }
 }
 
