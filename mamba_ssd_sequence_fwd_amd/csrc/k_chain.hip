@@ -191,18 +191,27 @@ __device__ __forceinline__ void state_tile(int i, f32x4 (&Y)[2][4], const bf16 *
 
 __device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int len, bf16 *y,
                                            size_t ystride, int lane) {
+  // Lanes 16 apart (same row) swap one p tile's worth of packed values so
+  // that each lane holds 8 consecutive p: 16-byte stores, 64 contiguous bytes
+  // per row and instruction.
+  const int lr = lane & 15, lg = lane >> 4, odd = lg & 1;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int l = 32 * i + 16 * u + (lane & 15);
-    if (l < len) {
-      bf16 *yr = y + (size_t)l * ystride + 4 * (lane >> 4);
+    const int l = 32 * i + 16 * u + lr;
+    uint2 pk[4];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        uint2 o;
-        o.x = pack2(Y[u][pt][0], Y[u][pt][1]);
-        o.y = pack2(Y[u][pt][2], Y[u][pt][3]);
-        *reinterpret_cast<uint2 *>(yr + 16 * pt) = o;
-      }
+    for (int pt = 0; pt < 4; ++pt) {
+      pk[pt].x = pack2(Y[u][pt][0], Y[u][pt][1]);
+      pk[pt].y = pack2(Y[u][pt][2], Y[u][pt][3]);
+    }
+    bf16 *yr = y + (size_t)l * ystride + 8 * (lg >> 1) + 16 * odd;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint2 keep = odd ? pk[2 * m + 1] : pk[2 * m];
+      const uint2 send = odd ? pk[2 * m] : pk[2 * m + 1];
+      const uint32_t rx = __shfl_xor(send.x, 16), ry = __shfl_xor(send.y, 16);
+      const uint4 o = odd ? make_uint4(rx, ry, keep.x, keep.y) : make_uint4(keep.x, keep.y, rx, ry);
+      if (l < len) *reinterpret_cast<uint4 *>(yr + 32 * m) = o;
     }
   }
 }
