@@ -117,13 +117,68 @@ __global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
 // with x in chunk_scan. Slot e of lane L holds s = 32 j + 16 (e / 4)
 // + 4 (L / 16) + (e % 4). Storage: [chunk][group][tile pair][half u][lane][8]
 // bf16, tile pair = i (i + 1) / 2 + j, half u = rows 16u..16u+15 of tile i.
-// One wave per (chunk, group, tile pair): every wave issues all its loads at
-// once and does 16 MFMAs. On the chain path the waves of the diagonal pairs
-// (j = i) also write B^T for the 32-token step i.
+// Two launch shapes, one wave per block:
+//   PAIRWISE: one wave per (chunk, group, tile pair), every load issued at
+//     once -- for small problems, where the grid would otherwise not fill
+//     the GPU;
+//   otherwise: one wave per (chunk, group, {i, T-1-i}), T+1 tile pairs each,
+//     C rows loaded once per row tile.
+// On the chain path the same kernel writes B^T in the A-operand layout of the
+// chunk-state product (tile (nt, ks), lane L: n = 16 nt + L%16, tokens
+// 32 ks + 8 (L/16) .. +7, zeros past the chunk end), transposing through LDS.
 // ============================================================================
-template <int N, int Q>
+template <int N>
+__device__ __forceinline__ void cb_pair(const bf16 *B, size_t ldr, int len, int j,
+                                        const bf16x8 (&cop)[2][N / 32], bf16 *dst) {
+  constexpr int KS = N / 32;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  bf16x8 bop[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bop[t][ks] = ldg8_row(B, ldr, 32 * j + 16 * t + lr, len, 32 * ks + 8 * lg);
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) acc[u][t] = mfma(bop[t][ks], cop[u][ks], acc[u][t]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    bf16x8 v;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * t + r] = (bf16)acc[u][t][r];
+    *reinterpret_cast<bf16x8 *>(dst + (size_t)u * 512 + lane * 8) = v;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void bt_step(const bf16 *B, size_t ldr, int len, int ks, int nks,
+                                        bf16 *btb, bf16 *sBt) {
+  const int lane = threadIdx.x & 63;
+  RowStager<N, 32, 64> st;
+  st.load(B, ldr, 32 * ks, len);
+  __syncthreads();  // a previous step's transposed reads are done
+  st.store(sBt);
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < N / 16; ++nt)
+    *reinterpret_cast<bf16x8 *>(btb + ((size_t)nt * nks + ks) * 512 + lane * 8) =
+        tr_operand<N>(sBt, 0, 16 * nt);
+}
+
+template <int N, int Q, bool PAIRWISE>
 __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
   constexpr int T = Q / 32, KS = N / 32, PAIRS = T * (T + 1) / 2;
+  __shared__ __attribute__((aligned(16))) bf16 sBt[32 * N];
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 16)
     reinterpret_cast<uint4 *>(a.zeros)[threadIdx.x] = make_uint4(0, 0, 0, 0);
   {
@@ -136,59 +191,46 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
   Chunk k;
   const int c = blockIdx.x;
   if (!chunk_of(a, c, k)) return;
-  const int g = blockIdx.y, pair = blockIdx.z;
-  int i = 0;
-  while ((i + 1) * (i + 2) / 2 <= pair) ++i;
-  const int j = pair - i * (i + 1) / 2;
+  const int g = blockIdx.y;
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const bf16 *C = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
   const bf16 *B = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
   const size_t ldr = (size_t)a.G * N;
-  bf16x8 cop[2][KS], bop[2][KS];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      cop[u][ks] = ldg8_row(C, ldr, 32 * i + 16 * u + lr, k.len, 32 * ks + 8 * lg);
-      bop[u][ks] = ldg8_row(B, ldr, 32 * j + 16 * u + lr, k.len, 32 * ks + 8 * lg);
-    }
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) acc[u][t] = mfma(bop[t][ks], cop[u][ks], acc[u][t]);
   bf16 *base = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512;
+  bf16 *btb =
+      a.bt ? static_cast<bf16 *>(a.bt) + ((size_t)c * a.G + g) * (N / 16) * T * 512 : nullptr;
+  if (PAIRWISE) {
+    const int pair = blockIdx.z;
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= pair) ++i;
+    const int j = pair - i * (i + 1) / 2;
+    bf16x8 cop[2][KS];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    bf16x8 v;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int ks = 0; ks < KS; ++ks)
+        cop[u][ks] = ldg8_row(C, ldr, 32 * i + 16 * u + lr, k.len, 32 * ks + 8 * lg);
+    cb_pair<N>(B, ldr, k.len, j, cop, base + (size_t)pair * 2 * 512);
+    if (btb && j == i) bt_step<N>(B, ldr, k.len, i, T, btb, sBt);
+  } else {
+    const int w = blockIdx.z;
+#pragma unroll 1
+    for (int ti = 0; ti < 2; ++ti) {
+      const int i = ti == 0 ? w : T - 1 - w;
+      bf16x8 cop[2][KS];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[4 * t + r] = (bf16)acc[u][t][r];
-    *reinterpret_cast<bf16x8 *>(base + (size_t)(pair * 2 + u) * 512 + lane * 8) = v;
-  }
-  // Chain path: B^T of this chunk and group in the A-operand layout of the
-  // chunk-state product (tile (nt, ks), lane L: n = 16 nt + L%16, tokens
-  // 32 ks + 8 (L/16) .. +7, zeros past the chunk end), step ks = i, by the
-  // diagonal pair's wave, transposing through LDS.
-  if (a.bt && j == i) {
-    __shared__ __attribute__((aligned(16))) bf16 sBt[32 * N];
-    bf16 *btb = static_cast<bf16 *>(a.bt) + ((size_t)c * a.G + g) * (N / 16) * (Q / 32) * 512;
-    const int ks = i;
-    RowStager<N, 32, 64> st;
-    st.load(B, ldr, 32 * ks, k.len);
-    st.store(sBt);
-    __syncthreads();
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int nt = 0; nt < N / 16; ++nt)
-      *reinterpret_cast<bf16x8 *>(btb + ((size_t)nt * (Q / 32) + ks) * 512 + lane * 8) =
-          tr_operand<N>(sBt, 0, 16 * nt);
+        for (int ks = 0; ks < KS; ++ks)
+          cop[u][ks] = ldg8_row(C, ldr, 32 * i + 16 * u + lr, k.len, 32 * ks + 8 * lg);
+#pragma unroll 1
+      for (int j = 0; j <= i; ++j)
+        cb_pair<N>(B, ldr, k.len, j, cop, base + (size_t)(i * (i + 1) / 2 + j) * 2 * 512);
+    }
+    if (btb) {
+#pragma unroll 1
+      for (int q = 0; q < 2; ++q) bt_step<N>(B, ldr, k.len, 2 * w + q, T, btb, sBt);
+    }
   }
 }
 
@@ -283,9 +325,14 @@ static hipError_t launch_nq(const Args &a, bf16 *cb, hipStream_t st, int which) 
   if (which == 0) {
     hipLaunchKernelGGL((k_chunk_state_mfma<N, Q>), dim3(a.nc_max, a.H), dim3(256), 0, st, a);
   } else if (which == 1) {
+    // Small problems: one wave per tile pair, so the grid fills the GPU.
     constexpr int T = Q / 32;
-    hipLaunchKernelGGL((k_chunk_cb<N, Q>), dim3(a.nc_max, a.G, T * (T + 1) / 2), dim3(64), 0, st,
-                       a, cb);
+    if ((int64_t)a.nc_max * a.G <= 256)
+      hipLaunchKernelGGL((k_chunk_cb<N, Q, true>), dim3(a.nc_max, a.G, T * (T + 1) / 2),
+                         dim3(64), 0, st, a, cb);
+    else
+      hipLaunchKernelGGL((k_chunk_cb<N, Q, false>), dim3(a.nc_max, a.G, Q / 64), dim3(64), 0, st,
+                         a, cb);
   } else {
     hipLaunchKernelGGL((k_chunk_scan_mfma<N, Q>), dim3(a.nc_max, a.H), dim3(Q), 0, st, a,
                        (const bf16 *)cb);
