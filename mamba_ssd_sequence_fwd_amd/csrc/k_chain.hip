@@ -217,16 +217,24 @@ __device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int le
 }
 
 // The state hand-off between workgroups that may sit on different XCDs
-// (each with its own L2). Ring entries are written and read with
-// device-scope atomic accesses, which are coherent across the whole GPU
-// without flushing or invalidating any cache: a producer's ring stores are
-// complete once its s_waitcnt vmcnt(0) returns, it then bumps the counter,
-// and a consumer issues its ring loads only after it has seen the counter.
-__device__ __forceinline__ void ring_store(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// (each with its own L2). Ring entries are written and read by 16-byte buffer
+// accesses with the sc1 cache policy (device scope, the same bits a relaxed
+// device-scope atomic access carries), which are coherent across the whole
+// GPU without flushing or invalidating any cache: a producer's ring stores
+// are complete once its s_waitcnt vmcnt(0) returns, it then bumps the
+// counter, and a consumer issues its ring loads only after it has seen the
+// counter. The counter alone orders the hand-off, so the entries need no
+// atomicity of their own.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kCachePolicyDevice = 16;  // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const float *slot, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(slot), (short)0, bytes, 0x00020000);
 }
-__device__ __forceinline__ float ring_load(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void ring_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCachePolicyDevice);
+}
+__device__ __forceinline__ f32x4 ring_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice));
 }
 
 // Bounded wait until the published-chunk counter reaches `want`. Returns
@@ -245,22 +253,21 @@ __device__ __forceinline__ bool wait_published(const int32_t *ctr, int want) {
 // Incoming state of head h, chunk k, in the state-tile layout of this wave
 // (tile (j, pt): rows n = 16 (nt0 + j) + 4(lane/16) + r, column p = 16 pt +
 // lane%16): the ring slot of the previous chunk, or at a sequence start the
-// initial state (or zeros). Ring slot layout: [wave][j][pt][r][lane], 256
-// contiguous bytes per access.
+// initial state (or zeros). Ring slot layout: [wave][j][pt][lane][r], one
+// 16-byte access per lane and 1 KB contiguous per wave access.
 template <int N, int NTW>
 __device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, const Chunk &k,
                                           int h, int wave, int nt0, int lane) {
   const size_t PN = (size_t)kP * N;
   const int lr = lane & 15, lg = lane >> 4;
   if (k.idx > 0) {
-    const float *rin =
-        a.ring + ((size_t)(k.seq * a.H + h) * 2 + ((k.idx + 1) & 1)) * PN + (size_t)wave * NTW * 4 * 256;
+    const __amdgpu_buffer_rsrc_t rin = ring_rsrc(
+        a.ring + ((size_t)(k.seq * a.H + h) * 2 + ((k.idx + 1) & 1)) * PN, (int)(PN * 4));
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hin[j][pt][r] = ring_load(rin + ((j * 4 + pt) * 4 + r) * 64 + lane);
+        hin[j][pt] = ring_load4(rin, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16));
   } else if (a.h0) {
     const float *h0 = a.h0 + (size_t)(k.seq * a.H + h) * PN;
 #pragma unroll
@@ -424,7 +431,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   chunks_of_seq(a, k.seq, cs0, cs1);
   const bool last = c + 1 >= cs1;
   const float dec = exp2_fast(cs_last);
-  float *rout = a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN + (size_t)wave * NTW * 4 * 256;
+  const __amdgpu_buffer_rsrc_t rout = ring_rsrc(a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN, (int)(PN * 4));
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
@@ -432,8 +439,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
       const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
       const f32x4 hout = dec * hin[j][pt] + hs[j][pt];
       if (!last) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ring_store(rout + ((j * 4 + pt) * 4 + r) * 64 + lane, hout[r]);
+        ring_store4(rout, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16), hout);
       } else if (a.hT) {
         *reinterpret_cast<float4 *>(a.hT + (size_t)pair * PN + (size_t)p * N + n) =
             make_float4(hout[0], hout[1], hout[2], hout[3]);
