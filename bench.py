@@ -33,6 +33,7 @@ import mamba_ssd_sequence_fwd_amd as ssd  # noqa: E402
 METRIC = "SSD fwd tokens/sec + % MFMA/HBM roofline at L=2048, H=80, P=64, N=128"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+COLD_EVICT_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
 MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
@@ -119,13 +120,13 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def cpu_baseline(inp: dict, w: si.Workload, budget_s: float) -> dict:
+def cpu_baseline(inp: dict, w: si.Workload, budget_s: float, threads: int = 0) -> dict:
     """Time the fp64 oracle (as it stands) on this host over the same workload:
     (sequence, head) pairs in a seeded random order, in batches, until the time
     budget is spent (the whole workload, repeated if it takes less than the
     budget); reported as tokens of the workload per second."""
     import oracle
-    threads = oracle.default_threads()
+    threads = threads or oracle.default_threads()
     lens = inp["seq_lens"] or [w.seqlen] * w.batch
     H = w.nheads
     x = inp["x"].reshape(-1, H, w.headdim)
@@ -167,6 +168,11 @@ def main():
     ap.add_argument("--per-sequence", action="store_true",
                     help="run the fused kernel with one workgroup per (sequence, head)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads for the oracle baseline (default: all this process may use)")
+    ap.add_argument("--cold", action="store_true",
+                    help="before every timed pass, write a 512 MiB buffer so that the pass "
+                         "starts with the Infinity Cache (MALL) and the L2s holding none of its data")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy "
                          "of this many MiB (known HBM traffic) to calibrate byte counters")
@@ -207,11 +213,25 @@ def main():
     # Timed region: K steps, every kernel bracketed by HIP events on the
     # stream the kernels run on; the call synchronises at the end.
     t0 = time.perf_counter()
-    times = plan.run_timed(args.steps, stream)
-    torch.cuda.synchronize()
+    if not args.cold:
+        times = plan.run_timed(args.steps, stream)
+        torch.cuda.synchronize()
+        per_kernel_ms = times.as_dict()
+        total_ms = per_kernel_ms.pop("_total_ms")
+    else:
+        # One pass at a time, each after an eviction write that the events
+        # do not cover; per-kernel and total times are summed over passes.
+        evict = torch.empty(COLD_EVICT_BYTES // 4, device=dev, dtype=torch.float32)
+        per_kernel_ms, total_ms = {}, 0.0
+        for i in range(args.steps):
+            evict.fill_(float(i))
+            t = plan.run_timed(1, stream).as_dict()
+            total_ms += t.pop("_total_ms")
+            for k, v in t.items():
+                per_kernel_ms[k] = per_kernel_ms.get(k, 0.0) + v / args.steps
+        torch.cuda.synchronize()
+        del evict
     wall = time.perf_counter() - t0
-    per_kernel_ms = times.as_dict()
-    total_ms = per_kernel_ms.pop("_total_ms")
     ms_per_step = total_ms / args.steps
     tokens = plan.tokens
     value = tokens / (ms_per_step / 1e3)
@@ -245,7 +265,8 @@ def main():
                    "seq_len": plan.prob.seqlen, "nheads": w.nheads, "headdim": w.headdim,
                    "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk,
                    "num_seqs": w.num_seqs, "tokens_per_step": tokens,
-                   "initial_state": inp["h0"] is not None},
+                   "initial_state": inp["h0"] is not None,
+                   "caches": "cold" if args.cold else "warm"},
         "roofline": roofline,
         "path": {"alg_bytes": int(path["bytes"]), "alg_flops": int(path["flops"]),
                  "GB/s": round(path["bytes"] / (ms_per_step * 1e-3) / 1e9, 1),
@@ -255,7 +276,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget, args.cpu_threads)
     print(json.dumps(out), flush=True)
 
 

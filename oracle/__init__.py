@@ -15,6 +15,9 @@ Two independent formulations of the same linear map:
   "Unifying SSM and attention": an SSM is multiplication by a semiseparable
   matrix, equivalently a masked attention whose mask is that matrix).
 
+A third module, :mod:`oracle.step`, is the decode step (one token of the
+recurrence per sequence, the state carried by the caller), in numpy.
+
 Every function here is plain and slow on purpose.
 """
 from __future__ import annotations
