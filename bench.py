@@ -86,6 +86,8 @@ def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
 TRAFFIC_PROFILES = {
     ("ssd_chain", "2.7b-bf16"): ("ssd_chain_2.7b-bf16_hbm_bytes.md",
                                  ("k_chain.hip", "mfma_common.h", "ssd_internal.h")),
+    ("ssd_step", "decode-2.7b-b256"): ("ssd_step_decode-2.7b-b256.md",
+                                       ("k_step.hip", "step.h", "ssd_internal.h")),
 }
 
 
@@ -156,6 +158,67 @@ def cpu_baseline(inp: dict, w: si.Workload, budget_s: float, threads: int = 0) -
                           done, w.name, len(order), done / len(order), elapsed, threads)}
 
 
+def bench_decode(args):
+    """Decode step: K back-to-back ssd_step calls on one state buffer (each
+    sequence advances one token per call), timed with HIP events on the
+    stream the kernel runs on. One kernel per step; it reads and writes the
+    whole fp32 state, so HBM bandwidth bounds it."""
+    batch, H, P, N, G = args.decode, 80, 64, 128, 1
+    inp = si.make_step_inputs(batch, H, P, N, G, "bf16", seed=4000)
+    dev = torch.device("cuda:0")
+    x, dt, B, C = (inp[k][0].to(dev) for k in ("x", "dt", "B", "C"))
+    A, D, state = inp["A"].to(dev), inp["D"].to(dev), inp["state"].to(dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream)
+    evict = torch.empty(COLD_EVICT_BYTES // 4, device=dev) if args.cold else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_ms = 0.0
+    if not args.cold:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        total_ms = e0.elapsed_time(e1)
+    else:
+        for i in range(args.steps):
+            evict.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            total_ms += e0.elapsed_time(e1)
+    wall = time.perf_counter() - t0
+    ms = total_ms / args.steps
+    e = 2
+    alg_bytes = batch * H * P * N * 4 * 2 + batch * (2 * H * P * e + H * e + 2 * G * N * e)
+    alg_flops = batch * H * P * N * 6
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "SSD decode step tokens/s (one token per sequence, one layer)",
+        "value": round(batch / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode-2.7b-b%d" % batch, "batch": batch, "nheads": H,
+                   "headdim": P, "dstate": N, "ngroups": G,
+                   "state_bytes": batch * H * P * N * 4,
+                   "caches": "cold" if args.cold else "warm"},
+        "roofline": {"kernel": "ssd_step", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("ssd_step", "decode-2.7b-b%d" % batch)},
+        "kernels": {"ssd_step": {"ms": round(ms, 5), "alg_bytes": alg_bytes,
+                                 "alg_flops": alg_flops, "GB/s": round(gbs, 1)}},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +233,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="host threads for the oracle baseline (default: all this process may use)")
+    ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
+                    help="instead of the forward pass, time the decode step (ssd_step) "
+                         "of BATCH sequences at the 2.7B shapes (H 80, P 64, N 128, bf16)")
     ap.add_argument("--cold", action="store_true",
                     help="before every timed pass, write a 512 MiB buffer so that the pass "
                          "starts with the Infinity Cache (MALL) and the L2s holding none of its data")
@@ -195,6 +261,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "launches": max(args.steps, 1)}), flush=True)
+        return
+
+    if args.decode:
+        bench_decode(args)
         return
 
     w = si.CONFIGS[args.config]

@@ -209,6 +209,43 @@ typedef struct ssd_workspace_layout {
 ssd_status ssd_get_workspace_layout(const ssd_problem *prob,
                                     ssd_workspace_layout *layout);
 
+/* One decode step: every sequence of a dense batch advances by one token,
+ * its fp32 state updated in place (the recurrent mode of the same layer).
+ *
+ * Per sequence b and head h, with group g = h / (nheads/ngroups):
+ *   state[b, h, p, n] = exp(dt[b, h] * A[h]) * state[b, h, p, n]
+ *                       + dt[b, h] * x[b, h, p] * B[b, g, n]
+ *   y[b, h, p]        = sum_n C[b, g, n] * state[b, h, p, n] + D[h] * x[b, h, p]
+ * i.e. one iteration of the recurrence ssd_forward evaluates, so a sequence
+ * may be prefilled with ssd_forward (final_state) and continued token by
+ * token here. Source: the discretised SSM evaluated as a recurrence
+ * (tj-hxxt.cn long read of the Mamba-1 paper, part II (1), "from continuous
+ * systems to discrete modelling") and the state cache that makes generation
+ * linear in length (same page, part IV (5), "computational efficiency", the
+ * inference-speed item).
+ *
+ * Arguments (device pointers owned by the caller, 16-byte aligned):
+ *   prob   batch = sequences (0 = nothing to do), seqlen must be 1,
+ *          num_seqs must be 0, flags must be 0; chunk_size is ignored.
+ *          nheads, headdim, dstate, ngroups and dtype as for ssd_forward
+ *          (headdim in {16, 32, 64, 128}, dstate a multiple of 16 up to 256).
+ *   x      (batch, H, P)   dtype
+ *   dt     (batch, H)      dtype, used as given (already positive)
+ *   A      (H)             fp32
+ *   B, C   (batch, G, N)   dtype
+ *   D      (H)             fp32, NULL = no skip term
+ *   state  (batch, H, P, N) fp32, read and overwritten with the new state
+ *   y      (batch, H, P)   dtype (out)
+ *   stream a hipStream_t (NULL = the default stream)
+ * The state must not overlap the other tensors. Errors: SSD_ERR_INVALID_ARG
+ * (malformed sizes, NULL or misaligned pointers), SSD_ERR_UNSUPPORTED (shape
+ * or dtype outside the set above), SSD_ERR_HIP (launch failed); nothing is
+ * enqueued on error. Enqueues one kernel; no allocation, no synchronisation,
+ * no workspace. */
+ssd_status ssd_step(const ssd_problem *prob, const void *x, const void *dt,
+                    const float *A, const void *B, const void *C, const float *D,
+                    float *state, void *y, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -64,7 +64,7 @@ class StageTimes(ctypes.Structure):
 
 
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-            "ssd_forward", "ssd_forward_timed", "ssd_get_workspace_layout",
+            "ssd_forward", "ssd_forward_timed", "ssd_step", "ssd_get_workspace_layout",
             "ssd_status_string", "ssd_last_error_detail")
 
 _lock = threading.Lock()
@@ -91,8 +91,9 @@ def load(path: str = LIB_PATH):
         lib.ssd_forward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
         lib.ssd_forward_timed.argtypes = ([P] + [vp] * 11 + [ctypes.c_size_t, vp, ctypes.c_int32,
                                           ctypes.POINTER(StageTimes)])
+        lib.ssd_step.argtypes = [P] + [vp] * 9
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed"):
+                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -257,3 +258,50 @@ def forward(x, dt, A, B, C, D=None, initial_state=None, chunk_size=256, cu_seqle
             **kw):
     """SSD forward pass: returns (y, final_state)."""
     return Plan(x, dt, A, B, C, D, initial_state, chunk_size, cu_seqlens, **kw).run()
+
+
+def step(x, dt, A, B, C, D=None, state=None, *, y=None, stream=None):
+    """One decode step (ssd_step): every sequence advances by one token and
+    ``state`` is updated IN PLACE; returns y.
+
+    Shapes: x (batch, H, P); dt (batch, H); A (H,) fp32; B, C (batch, G, N);
+    D (H,) fp32 or None; state (batch, H, P, N) fp32, contiguous; y (optional
+    output) like x. x, dt, B, C share the dtype (bfloat16 or float32).
+    """
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, nheads, headdim)")
+    batch, H, P = x.shape
+    if B.dim() != 3:
+        raise ValueError("B must be (batch, ngroups, dstate)")
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU (got %s)" % dev)
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be bfloat16 or float32")
+    for name, t, shape in (("dt", dt, (batch, H)), ("B", B, (batch, G, N)),
+                           ("C", C, (batch, G, N))):
+        if tuple(t.shape) != shape or t.dtype != x.dtype or t.device != dev:
+            raise ValueError("%s must be %s %s on %s" % (name, shape, x.dtype, dev))
+    if tuple(A.shape) != (H,) or A.dtype != torch.float32:
+        raise ValueError("A must be (H,) float32")
+    if D is not None and (tuple(D.shape) != (H,) or D.dtype != torch.float32):
+        raise ValueError("D must be (H,) float32")
+    if (state is None or tuple(state.shape) != (batch, H, P, N)
+            or state.dtype != torch.float32 or not state.is_contiguous()
+            or state.device != dev):
+        raise ValueError("state must be a contiguous (%d, %d, %d, %d) float32 tensor on %s"
+                         % (batch, H, P, N, dev))
+    if y is None:
+        y = torch.empty_like(x, memory_format=torch.contiguous_format)
+    elif tuple(y.shape) != (batch, H, P) or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("y must be a contiguous (%d, %d, %d) %s tensor" % (batch, H, P, x.dtype))
+    prob = make_problem(batch, 1, H, P, N, G, 0, 0, _DTYPES[x.dtype], 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    x, dt, A, B, C = (t.contiguous() for t in (x, dt, A, B, C))
+    D = D.contiguous() if D is not None else None
+    _check(load().ssd_step(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                           _ptr(D), _ptr(state), _ptr(y), ctypes.c_void_p(stream.cuda_stream)),
+           "ssd_step")
+    return y

@@ -28,6 +28,7 @@
 
 #include "ssd.h"
 #include "ssd_internal.h"
+#include "step.h"
 
 namespace {
 
@@ -441,6 +442,59 @@ ssd_status ssd_forward_timed(const ssd_problem *p, const void *x, const void *dt
   }
   for (auto &e : ev) (void)hipEventDestroy(e);
   return rc;
+}
+
+ssd_status ssd_step(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                    const void *B, const void *C, const float *D, float *state, void *y,
+                    void *stream) {
+  g_detail.clear();
+  if (!p) return fail(SSD_ERR_INVALID_ARG, "problem is NULL");
+  if (p->seqlen != 1)
+    return fail(SSD_ERR_INVALID_ARG, "a step advances one token: seqlen must be 1, got %d",
+                p->seqlen);
+  if (p->num_seqs != 0)
+    return fail(SSD_ERR_INVALID_ARG, "a step takes a dense batch: num_seqs must be 0, got %d",
+                p->num_seqs);
+  if (p->batch < 0 || p->nheads < 1 || p->headdim < 1 || p->dstate < 1 || p->ngroups < 1)
+    return fail(SSD_ERR_INVALID_ARG,
+                "sizes must be positive (batch %d >= 0, nheads %d headdim %d dstate %d "
+                "ngroups %d)", p->batch, p->nheads, p->headdim, p->dstate, p->ngroups);
+  if (p->nheads % p->ngroups != 0)
+    return fail(SSD_ERR_INVALID_ARG, "nheads %d not divisible by ngroups %d", p->nheads,
+                p->ngroups);
+  if (p->flags != 0) return fail(SSD_ERR_INVALID_ARG, "a step takes no flags (0x%x)", p->flags);
+  if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+  if (p->headdim != 16 && p->headdim != 32 && p->headdim != 64 && p->headdim != 128)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim %d not in {16, 32, 64, 128}", p->headdim);
+  if (p->dstate % 16 != 0 || p->dstate > 256)
+    return fail(SSD_ERR_UNSUPPORTED, "dstate %d not a multiple of 16 in [16, 256]", p->dstate);
+  ssd::StepArgs a{};
+  a.rows = (int64_t)p->batch * p->nheads * p->headdim;
+  a.H = p->nheads;
+  a.N = p->dstate;
+  a.G = p->ngroups;
+  a.heads_per_group = p->nheads / p->ngroups;
+  a.p_shift = __builtin_ctz((unsigned)p->headdim);
+  if ((int64_t)p->batch * p->nheads > INT32_MAX || ssd::step_blocks(a) > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "batch %d too large for one launch", p->batch);
+  if (p->batch == 0) return SSD_OK;
+  if (!x || !dt || !A || !B || !C || !state || !y)
+    return fail(SSD_ERR_INVALID_ARG, "x, dt, A, B, C, state and y must be non-NULL");
+  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(state))
+    return fail(SSD_ERR_INVALID_ARG, "x, B, C, y and state must be 16-byte aligned");
+  a.x = x;
+  a.dt = dt;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.state = state;
+  a.y = y;
+  if (ssd::launch_step(a, p->dtype == SSD_DTYPE_BF16, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return fail(SSD_ERR_HIP, "step kernel launch failed");
+  return SSD_OK;
 }
 
 }  // extern "C"

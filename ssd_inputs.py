@@ -15,6 +15,10 @@ to 256, so every input here is synthetic with those shapes):
   3   large-state-long   2      16384  64  64  256  8  256  bf16  (dt bias solved: mean exp(dt A) = 0.9)
   4   varlen-packed      64 sequences, lengths ~ U[16, 4096], packed; H 80, P 64, N 128, G 1, Q 256, bf16
 
+Decode steps (make_step_inputs): a dense batch of sequences advancing one token
+each, e.g. batch 8 or 256 at H 80, P 64, N 128, with the same value recipe and
+a random fp32 state ~ N(0, 0.1^2).
+
 Value recipe (all configs unless stated): x, B, C, D ~ N(0, 1);
 dt = softplus(z + bias) with z ~ N(0, 1) and bias = -2; A_h = -exp(U(0, 2));
 zero initial state. Draw order from numpy.random.default_rng(seed):
@@ -165,3 +169,27 @@ def scaled(w: Workload, **kw) -> Workload:
 def tokens(inp: dict) -> int:
     x = inp["x"]
     return int(x.shape[0] * x.shape[1])
+
+
+def make_step_inputs(batch: int, nheads: int, headdim: int, dstate: int, ngroups: int,
+                     dtype: str, seed: int, state_std: float = 0.1, steps: int = 1) -> dict:
+    """Seeded inputs of ``steps`` decode steps (one token per sequence each),
+    with the value recipe of the workloads above and a random fp32 state.
+
+    Draw order: x, B, C, z, u (for A), D, state. Returns x (steps, batch, H, P),
+    dt (steps, batch, H), B, C (steps, batch, G, N) in ``dtype``; A, D (H,)
+    fp32; state (batch, H, P, N) fp32.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((steps, batch, nheads, headdim), dtype=np.float32)
+    B = rng.standard_normal((steps, batch, ngroups, dstate), dtype=np.float32)
+    C = rng.standard_normal((steps, batch, ngroups, dstate), dtype=np.float32)
+    z = rng.standard_normal((steps, batch, nheads))
+    u = rng.uniform(0.0, 2.0, size=nheads)
+    D = rng.standard_normal(nheads)
+    state = rng.standard_normal((batch, nheads, headdim, dstate), dtype=np.float32) * np.float32(state_std)
+    return dict(x=_cast(x, dtype), dt=_cast(_softplus(z - 2.0), dtype),
+                A=torch.from_numpy((-np.exp(u)).astype(np.float32)),
+                B=_cast(B, dtype), C=_cast(C, dtype),
+                D=torch.from_numpy(D.astype(np.float32)),
+                state=torch.from_numpy(state))

@@ -153,3 +153,52 @@ def test_forward_rejects_bad_arguments_before_launch(lib):
 def test_status_strings(lib):
     for st in range(5):
         assert lib.ssd_status_string(st)
+
+
+def _step_status(lib, prob, ptrs=None):
+    """ssd_step's status for pointer values that are never dereferenced: each
+    case below is rejected (or is empty) before anything is enqueued."""
+    vp = ctypes.c_void_p
+    if ptrs is None:
+        ptrs = [vp(4096 * (i + 1)) for i in range(8)]   # 16-byte aligned, never touched
+    return lib.ssd_step(ctypes.byref(prob), *ptrs, vp(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"seqlen": 2}, ssd.SSD_ERR_INVALID_ARG),
+    ({"seqlen": 0}, ssd.SSD_ERR_INVALID_ARG),
+    ({"batch": 1, "num_seqs": 1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"batch": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"nheads": 0}, ssd.SSD_ERR_INVALID_ARG),
+    ({"ngroups": 3}, ssd.SSD_ERR_INVALID_ARG),
+    ({"flags": ssd.SSD_FLAG_UNFUSED}, ssd.SSD_ERR_INVALID_ARG),
+    ({"dtype": 7}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"headdim": 48}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 24}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 272}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"batch": 2 ** 30, "nheads": 8}, ssd.SSD_ERR_UNSUPPORTED),   # batch * H above 32 bits
+])
+def test_step_validate(lib, kw, status):
+    kw = dict({"seqlen": 1}, **kw)
+    assert _step_status(lib, P(**kw)) == status
+
+
+def test_step_empty_batch_is_a_no_op(lib):
+    # batch 0: nothing to do, no pointer needed and nothing enqueued
+    prob = P(seqlen=1, batch=0)
+    assert _step_status(lib, prob, [ctypes.c_void_p(None)] * 8) == ssd.SSD_OK
+
+
+def test_step_rejects_null_and_misaligned_pointers(lib):
+    prob = P(seqlen=1)
+    vp = ctypes.c_void_p
+    good = [vp(4096 * (i + 1)) for i in range(8)]
+    for i in (0, 1, 2, 3, 4, 6, 7):          # every pointer but D is required
+        ptrs = list(good)
+        ptrs[i] = vp(None)
+        assert _step_status(lib, prob, ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    for i in (0, 3, 4, 6, 7):                # x, B, C, state, y: 16-byte aligned
+        ptrs = list(good)
+        ptrs[i] = vp(4096 * (i + 1) + 8)
+        assert _step_status(lib, prob, ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    assert "aligned" in lib.ssd_last_error_detail().decode()
