@@ -13,9 +13,10 @@
 // published-chunk counter. Per workgroup (four waves), with cs the log2-decay
 // prefix of dt*A inside the chunk:
 //
-//   1. ticket -> (chunk, head); x of the chunk into LDS (direct global->LDS),
-//      dt, the chunk's B^T operand tiles into registers; the decay tables
-//      (cs, w, u) by a wavefront prefix.
+//   1. ticket -> (chunk, head); dt, the chunk's first B^T operand tiles and
+//      x into registers (loads complete in issue order, so x is waited for
+//      step by step); the decay tables (cs, w, u) by a wavefront prefix; the
+//      first half of x into LDS (the second half halfway through step 2).
 //   2. S_c = (w o B)^T x (w_s = 2^(cs_last - cs_s) dt_s): the chunk's own
 //      state from a zero start (the chunk_state step).
 //   3. h_in from the previous chunk's workgroup (loaded while step 2 runs when
@@ -39,7 +40,12 @@
 // LDS holds only x (the operand both products read transposed) and h_in
 // (bf16), 52 KB at chunk 256, so three workgroups share a CU. Each wave owns
 // whole 32-row output tiles, so the two 16-row halves of a tile share every
-// x and h_in read.
+// x and h_in read. x is staged through registers rather than copied
+// global->LDS directly: while such a copy is pending, every wait on a
+// register load drains all outstanding loads, which would serialise the
+// prefetches. Within each 32-token step, the small LDS reads go first and the
+// x operand reads right after, so their latency hides behind the scaling
+// arithmetic (LDS returns in order).
 //
 // HBM traffic: x, y once; B, C, dt and the C B^T tiles once per head
 // through L2; 32 KB of fp32 state written and read per (chunk, head).
@@ -90,9 +96,19 @@ __device__ __forceinline__ void intra_tile(int i, f32x4 (&Y)[2][4], const bf16 *
       m0[u] = m1[u];
       m1[u] = ldg8(cbase + (size_t)((pair0 + min(j + 2, i)) * 2 + u) * 512);
     }
-    const float e_r0 = exp2_fast(cs_r0 - sCs[32 * j + 31]);
+    // LDS reads first (they return in order): the decay inputs, then every
+    // x operand of the step, whose latency the scaling below then hides.
+    const float cs_e = sCs[32 * j + 31];
     const float4 ua = *reinterpret_cast<const float4 *>(sU + 32 * j + 4 * lg);
     const float4 ub = *reinterpret_cast<const float4 *>(sU + 32 * j + 16 + 4 * lg);
+    bf16x8 xv[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const bf16x4 lo = ds_tr4(sX, 32 * j * kP + xoff[pt]);
+      const bf16x4 hi = ds_tr4(sX, (32 * j + 16) * kP + xoff[pt]);
+      xv[pt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    const float e_r0 = exp2_fast(cs_r0 - cs_e);
     const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -101,13 +117,9 @@ __device__ __forceinline__ void intra_tile(int i, f32x4 (&Y)[2][4], const bf16 *
       for (int e = 0; e < 8; ++e) m[u][e] = (bf16)((float)m[u][e] * (fa * uu[e]));
     }
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const bf16x4 lo = ds_tr4(sX, 32 * j * kP + xoff[pt]);
-      const bf16x4 hi = ds_tr4(sX, (32 * j + 16) * kP + xoff[pt]);
-      const bf16x8 xv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(xv, m[u], Y[u][pt]);
-    }
+      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(xv[pt], m[u], Y[u][pt]);
   }
   // Diagonal tile j = i (m0 holds it: the stream clamps at i).
   {
@@ -170,15 +182,12 @@ __device__ __forceinline__ void state_tile(int i, f32x4 (&Y)[2][4], const bf16 *
     for (int pt = 0; pt < 4; ++pt) Y[u][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < N / 32; ++ks) {
-    bf16x8 acv[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) acv[u] = 32 * i + 16 * u + lr < len ? ac[u][ks] : zero8();
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       const bf16x8 bh = *reinterpret_cast<const bf16x8 *>(
           sH + hbase + swz<N>(16 * pt + lr, 32 * ks + 8 * lg));
 #pragma unroll
-      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(bh, acv[u], Y[u][pt]);
+      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(bh, ac[u][ks], Y[u][pt]);
     }
   }
 #pragma unroll
@@ -191,26 +200,27 @@ __device__ __forceinline__ void state_tile(int i, f32x4 (&Y)[2][4], const bf16 *
 
 __device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int len, bf16 *y,
                                            size_t ystride, int lane) {
-  // Lanes 16 apart (same row) swap one p tile's worth of packed values so
-  // that each lane holds 8 consecutive p: 16-byte stores, 64 contiguous bytes
-  // per row and instruction.
-  const int lr = lane & 15, lg = lane >> 4, odd = lg & 1;
+  // Lanes 16 apart (same row l) exchange one p tile's worth of packed values
+  // so that each lane holds 8 consecutive p: 16-byte stores, 64 contiguous
+  // bytes per row and instruction. v_permlane16_swap swaps the odd 16-lane
+  // rows of its first operand with the even rows of its second, so after
+  // swapping (p tile 2m, p tile 2m+1) every lane holds its output in order.
+  const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int l = 32 * i + 16 * u + lr;
-    uint2 pk[4];
+    uint32_t pk[4][2];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-      pk[pt].x = pack2(Y[u][pt][0], Y[u][pt][1]);
-      pk[pt].y = pack2(Y[u][pt][2], Y[u][pt][3]);
+      pk[pt][0] = pack2(Y[u][pt][0], Y[u][pt][1]);
+      pk[pt][1] = pack2(Y[u][pt][2], Y[u][pt][3]);
     }
-    bf16 *yr = y + (size_t)l * ystride + 8 * (lg >> 1) + 16 * odd;
+    bf16 *yr = y + (size_t)l * ystride + 8 * (lg >> 1) + 16 * (lg & 1);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const uint2 keep = odd ? pk[2 * m + 1] : pk[2 * m];
-      const uint2 send = odd ? pk[2 * m] : pk[2 * m + 1];
-      const uint32_t rx = __shfl_xor(send.x, 16), ry = __shfl_xor(send.y, 16);
-      const uint4 o = odd ? make_uint4(rx, ry, keep.x, keep.y) : make_uint4(keep.x, keep.y, rx, ry);
+      const auto sx = __builtin_amdgcn_permlane16_swap(pk[2 * m][0], pk[2 * m + 1][0], false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(pk[2 * m][1], pk[2 * m + 1][1], false, false);
+      const uint4 o = make_uint4(sx[0], sy[0], sx[1], sy[1]);
       if (l < len) *reinterpret_cast<uint4 *>(yr + 32 * m) = o;
     }
   }
@@ -330,7 +340,24 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N, PN = (size_t)kP * N;
   const bf16 *xc = static_cast<const bf16 *>(a.x) + (size_t)k.start * ldx + (size_t)h * kP;
   const bf16 *cc = static_cast<const bf16 *>(a.C) + (size_t)k.start * ldb + (size_t)g * N;
-  async_rows<kP, Q, kChainWaves>(sX, xc, ldx, k.len, lane);
+  // Loads in the order they are needed (vector memory loads complete in
+  // issue order): dt, the predecessor poll, the first B^T tiles, then x into
+  // registers, one instruction per 32-token step (instruction k of wave w:
+  // rows 32k + 8w + lane/8, 16 bytes each). x reaches LDS step by step, so
+  // S_c starts once the first half has arrived.
+  float dtv;
+  {
+    const int t = min(tid, k.len - 1);
+    const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
+    dtv = tid < k.len ? d : 0.f;  // zero past the chunk end (and for tid >= Q)
+  }
+  const int pair = k.seq * a.H + h;
+  const bool first = k.idx == 0;
+  int early = 0;  // published count of the predecessor, read early
+  if (!first && tid == 0)
+    early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float ah = a.A[h] * kLog2eChain;
+  const float dsk = a.D ? a.D[h] : 0.f;
   const int nt0 = wave * NTW;
   // This wave's B^T operand tiles (n tiles nt0..), streamed KPF 32-token
   // steps ahead of their use; the first KPF steps now.
@@ -341,19 +368,23 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
     for (int ks = 0; ks < KPF; ++ks) bts[j][ks] = ldg8(btc + (size_t)(j * NKS + ks) * 512);
-  const int pair = k.seq * a.H + h;
-  const bool first = k.idx == 0;
-  int early = 0;  // published count of the predecessor, read early
-  if (!first && tid == 0)
-    early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float dtv;
+  const int xrl = lane >> 3, xcol = lane & 7;
+  bf16x8 xr[NKS];
   {
-    const int t = min(tid, k.len - 1);
-    const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
-    dtv = tid < k.len ? d : 0.f;  // zero past the chunk end (and for tid >= Q)
+    const char *xb = reinterpret_cast<const char *>(xc);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int r = 32 * ks + 8 * wave + xrl;
+      xr[ks] = *reinterpret_cast<const bf16x8 *>(
+          xb + (uint32_t)min(r, k.len - 1) * (uint32_t)(ldx * 2) + 16u * (uint32_t)xcol);
+    }
   }
-  const float ah = a.A[h] * kLog2eChain;
-  const float dsk = a.D ? a.D[h] : 0.f;
+  // x rows of step ks into the swizzled LDS tile (rows past len hold copies
+  // of the last row: finite values that are multiplied by zero weights).
+  auto put_x = [&](int ks) {
+    const int r = 32 * ks + 8 * wave + xrl;
+    *reinterpret_cast<bf16x8 *>(sX + r * kP + ((xcol ^ (r & 7)) << 3)) = xr[ks];
+  };
   const float incl = wave_inclusive_sum(dtv * ah);
   if (lane == 63 && wave < Q / 64) sTot[wave] = incl;
   if (tid == 0) sReady = (first || early >= k.idx) ? 1 : 0;
@@ -374,7 +405,9 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     sW[tid] = exp2_fast(cs_last - cst) * dtv;
     sU[tid] = exp2_fast(cs_tile_end - cst) * dtv;
   }
-  wait_vmem_all();  // x has landed
+  constexpr int XH = NKS / 2;  // x steps in LDS before S_c starts
+#pragma unroll
+  for (int ks = 0; ks < XH; ++ks) put_x(ks);
   __syncthreads();
 
   // ---- 2. S_c = (w o B)^T x; h_in loads in flight when already published ------
@@ -395,9 +428,22 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   }
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
+    if (ks == XH) {  // second half of x
+#pragma unroll
+      for (int k2 = XH; k2 < NKS; ++k2) put_x(k2);
+      __syncthreads();
+    }
     const int s0 = 32 * ks;
+    // LDS reads first (in-order return): the weights, then the x operands.
     const float4 wa = *reinterpret_cast<const float4 *>(sW + s0 + 8 * lg);
     const float4 wb = *reinterpret_cast<const float4 *>(sW + s0 + 8 * lg + 4);
+    bf16x8 xv[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const bf16x4 xl = ds_tr4(sX, s0 * kP + xoff[pt][0]);
+      const bf16x4 xh = ds_tr4(sX, s0 * kP + xoff[pt][1]);
+      xv[pt] = bf16x8{xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+    }
     const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
     bf16x8 av[NTW];
 #pragma unroll
@@ -407,13 +453,9 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
       if (ks + KPF < NKS) bts[j][ks % KPF] = ldg8(btc + (size_t)(j * NKS + ks + KPF) * 512);
     }
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const bf16x4 xl = ds_tr4(sX, s0 * kP + xoff[pt][0]);
-      const bf16x4 xh = ds_tr4(sX, s0 * kP + xoff[pt][1]);
-      const bf16x8 xv = {xl[0], xl[1], xl[2], xl[3], xh[0], xh[1], xh[2], xh[3]};
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) hs[j][pt] = mfma(av[j], xv, hs[j][pt]);
-    }
+      for (int j = 0; j < NTW; ++j) hs[j][pt] = mfma(av[j], xv[pt], hs[j][pt]);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -458,11 +500,11 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   bf16 *yc = static_cast<bf16 *>(a.y) + (size_t)k.start * ldx + (size_t)h * kP;
   bf16x8 acB[2][N / 32];
-  if (NTILE == 2) load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);  // in flight during tile A
   {
     f32x4 Y[2][4];
     state_tile<N>(iA, Y, sH, sCs, acA, k.len, lane);
     intra_tile<Q>(iA, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
+    if (NTILE == 2) load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);  // in flight during the stores
     store_tile(iA, Y, k.len, yc, ldx, lane);
   }
   if (NTILE == 2) {
