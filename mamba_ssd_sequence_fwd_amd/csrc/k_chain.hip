@@ -297,13 +297,14 @@ __device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, c
 }
 
 template <int N, int Q>
-__global__ __launch_bounds__(64 * kChainWaves) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(64 * kChainWaves)
+__attribute__((amdgpu_waves_per_eu(N == 256 ? 2 : 3, N == 256 ? 2 : 3)))
 void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   constexpr int T = Q / 32, PAIRS = T * (T + 1) / 2, NKS = Q / 32;
   constexpr int NTW = N / 64;                 // 16-row n tiles of the state per wave
   constexpr int NTILE = T == 8 ? 2 : 1;       // 32-row output tiles per wave
   static_assert(Q == 128 || Q == 256, "chain kernel: chunk 128 or 256");
-  static_assert(N == 64 || N == 128, "chain kernel: N 64 or 128");
+  static_assert(N == 64 || N == 128 || N == 256, "chain kernel: N 64, 128 or 256");
   __shared__ __attribute__((aligned(16))) bf16 sX[Q * kP];  // x, [token][p]
   __shared__ __attribute__((aligned(16))) bf16 sH[kP * N];  // h_in (bf16), [p][n]
   __shared__ __attribute__((aligned(16))) float sCs[Q];
@@ -536,7 +537,8 @@ hipError_t launch_final_of_empty(const Args &a, hipStream_t st) {
 }
 
 bool chain_path_supports(const Args &a) {
-  return mfma_path_supports(a) && (a.Q == 128 || a.Q == 256) && (a.N == 64 || a.N == 128);
+  return mfma_path_supports(a) && (a.Q == 128 || a.Q == 256) &&
+         (a.N == 64 || a.N == 128 || a.N == 256);
 }
 
 template <int N, int Q>
@@ -553,6 +555,9 @@ hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream
   if (a.N == 64)
     return a.Q == 128 ? launch_chain_nq<64, 128>(a, cb, bt, st)
                       : launch_chain_nq<64, 256>(a, cb, bt, st);
+  if (a.N == 256)
+    return a.Q == 128 ? launch_chain_nq<256, 128>(a, cb, bt, st)
+                      : launch_chain_nq<256, 256>(a, cb, bt, st);
   return a.Q == 128 ? launch_chain_nq<128, 128>(a, cb, bt, st)
                     : launch_chain_nq<128, 256>(a, cb, bt, st);
 }

@@ -31,6 +31,10 @@ SMALL = {
     "S2-a-zero": si.scaled(S["S2"], batch=1, seqlen=800, nheads=4, seed=2012),
     "S3-varlen-slow": si.scaled(S["S3"], nheads=4, num_seqs=5, len_range=(100, 900),
                                 seed=2013),
+    "S1-N256-h0": si.scaled(S["S1"], batch=2, seqlen=700, nheads=4, dstate=256, ngroups=2,
+                            seed=2014),
+    "S1-N256-Q128": si.scaled(S["S1"], batch=1, seqlen=650, nheads=4, dstate=256, chunk=128,
+                              seed=2015),
     "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
                               chunk=128, seed=2021),
     "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
