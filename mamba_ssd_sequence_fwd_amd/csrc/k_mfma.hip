@@ -127,17 +127,13 @@ __global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
 // chunk-state product (tile (nt, ks), lane L: n = 16 nt + L%16, tokens
 // 32 ks + 8 (L/16) .. +7, zeros past the chunk end), transposing through LDS.
 // ============================================================================
+// Product of one tile pair from its operands: bop = B rows 32j + 16t + lr,
+// cop = C rows 32i + 16u + lr (both: columns 32ks + 8 (L/16) .. +7).
 template <int N>
-__device__ __forceinline__ void cb_pair(const bf16 *B, size_t ldr, int len, int j,
-                                        const bf16x8 (&cop)[2][N / 32], bf16 *dst) {
+__device__ __forceinline__ void cb_pair_ops(const bf16x8 (&bop)[2][N / 32],
+                                            const bf16x8 (&cop)[2][N / 32], bf16 *dst) {
   constexpr int KS = N / 32;
-  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  bf16x8 bop[2][KS];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bop[t][ks] = ldg8_row(B, ldr, 32 * j + 16 * t + lr, len, 32 * ks + 8 * lg);
+  const int lane = threadIdx.x & 63;
   f32x4 acc[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -158,6 +154,21 @@ __device__ __forceinline__ void cb_pair(const bf16 *B, size_t ldr, int len, int 
       for (int r = 0; r < 4; ++r) v[4 * t + r] = (bf16)acc[u][t][r];
     *reinterpret_cast<bf16x8 *>(dst + (size_t)u * 512 + lane * 8) = v;
   }
+}
+
+
+template <int N>
+__device__ __forceinline__ void cb_pair(const bf16 *B, size_t ldr, int len, int j,
+                                        const bf16x8 (&cop)[2][N / 32], bf16 *dst) {
+  constexpr int KS = N / 32;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  bf16x8 bop[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bop[t][ks] = ldg8_row(B, ldr, 32 * j + 16 * t + lr, len, 32 * ks + 8 * lg);
+  cb_pair_ops<N>(bop, cop, dst);
 }
 
 template <int N>
@@ -230,6 +241,78 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
     if (btb) {
 #pragma unroll 1
       for (int q = 0; q < 2; ++q) bt_step<N>(B, ldr, k.len, 2 * w + q, T, btb, sBt);
+    }
+  }
+}
+
+// Large problems: one 4-wave workgroup per (chunk, group). The chunk's B
+// rows are copied into LDS once (row-major, swizzled; rows past the chunk end
+// are zero); wave w computes the tile pairs of its row tiles (w and T-1-w at
+// chunk 256, w at chunk 128) from C rows in registers and B tiles read from
+// LDS, and writes its share of the B^T operand tiles by transposed reads of
+// the same copy. B and C are each read once per (chunk, group).
+template <int N, int Q>
+__global__ __launch_bounds__(256) void k_chunk_cb_staged(Args a, bf16 *cb) {
+  constexpr int T = Q / 32, KS = N / 32, PAIRS = T * (T + 1) / 2, NRT = T / 4;
+  static_assert(T == 4 || T == 8, "staged C B^T: chunk 128 or 256");
+  __shared__ __attribute__((aligned(16))) bf16 sB[Q * N];
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 16)
+    reinterpret_cast<uint4 *>(a.zeros)[threadIdx.x] = make_uint4(0, 0, 0, 0);
+  {
+    // Chain path: clear the ticket, error word and published-chunk counters
+    // for the kernel that follows on the stream.
+    const int nb = gridDim.x * gridDim.y;
+    const int b = blockIdx.x + gridDim.x * blockIdx.y;
+    for (int i = b * 256 + threadIdx.x; i < a.nsync; i += nb * 256) a.sync[i] = 0;
+  }
+  Chunk k;
+  const int c = blockIdx.x;
+  if (!chunk_of(a, c, k)) return;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bf16 *C = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
+  const bf16 *B = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
+  const size_t ldr = (size_t)a.G * N;
+  bf16 *base = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512;
+  {
+    RowStager<N, Q, 256> st;
+    st.load(B, ldr, 0, k.len);
+    st.store(sB);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int ti = 0; ti < NRT; ++ti) {
+    const int i = ti == 0 ? wave : T - 1 - wave;
+    bf16x8 cop[2][KS];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        cop[u][ks] = ldg8_row(C, ldr, 32 * i + 16 * u + lr, k.len, 32 * ks + 8 * lg);
+#pragma unroll 1
+    for (int j = 0; j <= i; ++j) {
+      bf16x8 bop[2][KS];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          bop[t][ks] = *reinterpret_cast<const bf16x8 *>(
+              sB + rswz<N>(32 * j + 16 * t + lr, 32 * ks + 8 * lg));
+      cb_pair_ops<N>(bop, cop, base + (size_t)(i * (i + 1) / 2 + j) * 2 * 512);
+    }
+  }
+  if (a.bt) {
+    // B^T operand tiles (nt, ks): this wave's n tiles, every 32-token step.
+    bf16 *btb = static_cast<bf16 *>(a.bt) + ((size_t)c * a.G + g) * (N / 16) * T * 512;
+    constexpr int NTW = N / 64;
+#pragma unroll 1
+    for (int q = 0; q < NTW; ++q) {
+      const int nt = wave * NTW + q;
+#pragma unroll
+      for (int ks = 0; ks < T; ++ks)
+        *reinterpret_cast<bf16x8 *>(btb + ((size_t)nt * T + ks) * 512 + lane * 8) =
+            tr_operand<N>(sB, 32 * ks, 16 * nt);
     }
   }
 }
@@ -330,6 +413,9 @@ static hipError_t launch_nq(const Args &a, bf16 *cb, hipStream_t st, int which) 
     if ((int64_t)a.nc_max * a.G <= 256)
       hipLaunchKernelGGL((k_chunk_cb<N, Q, true>), dim3(a.nc_max, a.G, T * (T + 1) / 2),
                          dim3(64), 0, st, a, cb);
+    else if (Q >= 128)
+      hipLaunchKernelGGL((k_chunk_cb_staged<N, (Q >= 128 ? Q : 128)>), dim3(a.nc_max, a.G),
+                         dim3(256), 0, st, a, cb);
     else
       hipLaunchKernelGGL((k_chunk_cb<N, Q, false>), dim3(a.nc_max, a.G, Q / 64), dim3(64), 0, st,
                          a, cb);

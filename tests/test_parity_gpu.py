@@ -35,6 +35,10 @@ SMALL = {
                             seed=2014),
     "S1-N256-Q128": si.scaled(S["S1"], batch=1, seqlen=650, nheads=4, dstate=256, chunk=128,
                               seed=2015),
+    # 65 chunks x 4 groups: more than 256 (chunk, group) pairs, so the C B^T
+    # kernel stages each chunk's B in LDS
+    "staged-cb-G4-N64": si.scaled(C[3], batch=1, seqlen=16500, nheads=8, ngroups=4,
+                                  dstate=64, seed=2025),
     "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
                               chunk=128, seed=2021),
     "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
