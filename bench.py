@@ -219,6 +219,73 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+# Vector-ALU ceiling of the selective scan, from unit counts and clock: every
+# (token, channel, state) element needs one exp2 (a transcendental, issued at
+# a quarter of the full rate) and two FMAs, i.e. 6 full-rate lane-slots; a
+# SIMD issues 16 lane-slots per cycle; 256 CUs x 4 SIMDs at 2.4 GHz.
+SCAN_PEAK_ELEMS = 256 * 4 * 16 * 2.4e9 / 6
+
+
+def bench_scan(args):
+    """Mamba-1 selective scan: K back-to-back launches over the same inputs,
+    timed with HIP events on the stream the kernel runs on."""
+    batch, L, Dm, N = 8, 2048, 5120, args.scan
+    inp = si.make_scan_inputs(batch, L, Dm, N, "bf16", seed=4100, h0_std=0.1)
+    dev = torch.device("cuda:0")
+    d = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    y = torch.empty_like(d["x"])
+    hT = torch.empty((batch, Dm, N), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    run = lambda: ssd.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                                     y=y, final_state=hT, stream=stream)
+    for _ in range(args.warmup):
+        run()
+    evict = torch.empty(COLD_EVICT_BYTES // 4, device=dev) if args.cold else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_ms = 0.0
+    if not args.cold:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+        total_ms = e0.elapsed_time(e1)
+    else:
+        for i in range(args.steps):
+            evict.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            e1.synchronize()
+            total_ms += e0.elapsed_time(e1)
+    wall = time.perf_counter() - t0
+    ms = total_ms / args.steps
+    elems = batch * L * Dm * N
+    alg_bytes = batch * L * (3 * Dm * 2 + 2 * N * 2) + Dm * N * 4 + 2 * batch * Dm * N * 4
+    achieved = elems / (ms * 1e-3)
+    out = {
+        "metric": "Mamba-1 selective scan tokens/s (the SSD layer's comparator)",
+        "value": round(batch * L / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mamba1-scan-2.7b-N%d" % N, "batch": batch, "seq_len": L,
+                   "dim": Dm, "dstate": N, "caches": "cold" if args.cold else "warm"},
+        "roofline": {"kernel": "selective_scan", "bound": "alu",
+                     "achieved": round(achieved / 1e9, 1), "peak": round(SCAN_PEAK_ELEMS / 1e9, 1),
+                     "unit": "Gelem/s", "frac": round(achieved / SCAN_PEAK_ELEMS, 4),
+                     "traffic": None},
+        "kernels": {"selective_scan": {"ms": round(ms, 5), "alg_bytes": alg_bytes,
+                                       "GB/s": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                                       "elements": elems}},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +303,10 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="BATCH",
                     help="instead of the forward pass, time the decode step (ssd_step) "
                          "of BATCH sequences at the 2.7B shapes (H 80, P 64, N 128, bf16)")
+    ap.add_argument("--scan", type=int, default=0, metavar="N",
+                    help="instead of the SSD forward pass, time the Mamba-1 selective scan "
+                         "(ssd_selective_scan) at the 2.7B shapes (batch 8, 2048 tokens, 5120 "
+                         "channels) with state size N per channel")
     ap.add_argument("--cold", action="store_true",
                     help="before every timed pass, write a 512 MiB buffer so that the pass "
                          "starts with the Infinity Cache (MALL) and the L2s holding none of its data")
@@ -265,6 +336,9 @@ def main():
 
     if args.decode:
         bench_decode(args)
+        return
+    if args.scan:
+        bench_scan(args)
         return
 
     w = si.CONFIGS[args.config]

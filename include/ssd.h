@@ -246,6 +246,45 @@ ssd_status ssd_step(const ssd_problem *prob, const void *x, const void *dt,
                     const float *A, const void *B, const void *C, const float *D,
                     float *state, void *y, void *stream);
 
+/* The Mamba-1 selective scan: the layer that SSD is measured against. Its A
+ * is a diagonal N x D matrix (one rate per channel and state index) instead
+ * of one scalar per head, so it cannot use matrix products; the pages credit
+ * Mamba-2's restriction with a 2-8x speed-up over this scan (QbitAI CSDN
+ * repost, abstract; briefgpt TL;DR). The step, B and C depend on the input
+ * and A is discretised as exp(step * A) (tj-hxxt.cn long read of the Mamba-1
+ * paper, part III (2) and item 3); A's shape N x D and the step's B x L x D
+ * follow the kuaisou snippet on selective SSMs as linear attention. Per
+ * sequence b, channel d and state index n:
+ *   h[b, d, n] <- exp(delta[b, t, d] * A[d, n]) * h[b, d, n]
+ *                 + delta[b, t, d] * B[b, t, n] * x[b, t, d]
+ *   y[b, t, d]  = sum_n C[b, t, n] * h[b, d, n] + D[d] * x[b, t, d]
+ * With A[d, n] = A_h for the channels of head h and delta shared by them it
+ * is the SSD operation above.
+ *
+ * Problem: batch >= 0 (0 = nothing to do), seqlen >= 0, dim a multiple of 64,
+ * dstate in {16, 32, 64, 128, 256}, batch <= 65535, flags 0.
+ * Arguments (device pointers owned by the caller, 16-byte aligned):
+ *   x, delta       (batch, seqlen, dim)   dtype; delta used as given (> 0)
+ *   A              (dim, dstate) fp32
+ *   B, C           (batch, seqlen, dstate) dtype (one set for all channels)
+ *   D              (dim) fp32, NULL = no skip term
+ *   initial_state  (batch, dim, dstate) fp32, NULL = zeros
+ *   y              (batch, seqlen, dim) dtype (out)
+ *   final_state    (batch, dim, dstate) fp32 (out), NULL = not written
+ *   stream         a hipStream_t (NULL = the default stream)
+ * Errors: SSD_ERR_INVALID_ARG (malformed sizes, NULL or misaligned
+ * pointers), SSD_ERR_UNSUPPORTED (outside the set above), SSD_ERR_HIP;
+ * nothing is enqueued on error. One kernel, no allocation, no workspace. */
+typedef struct ssd_scan_problem {
+  int32_t batch, seqlen, dim, dstate;
+  ssd_dtype dtype;
+  uint32_t flags;
+} ssd_scan_problem;
+ssd_status ssd_selective_scan(const ssd_scan_problem *prob, const void *x, const void *delta,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const float *initial_state, void *y, float *final_state,
+                              void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -7,9 +7,11 @@ with ``python -m mamba_ssd_sequence_fwd_amd.build``.
     y, final_state = forward(x, dt, A, B, C, D, initial_state, chunk_size=256,
                              cu_seqlens=None)
     y_t = step(x_t, dt_t, A, B_t, C_t, D, state)   # one decode step, state in place
+    y, h = selective_scan(x, delta, A, B, C, D)     # the Mamba-1 scan (comparator)
 """
 from ._lib import (  # noqa: F401
-    EXPORTED, LIB_PATH, Plan, Problem, SSDError, StageTimes, WorkspaceLayout, forward, load,
+    EXPORTED, LIB_PATH, Plan, Problem, ScanProblem, SSDError, StageTimes, WorkspaceLayout,
+    forward, load, selective_scan,
     make_problem, step, validate, validate_cu_seqlens, workspace_layout, workspace_size,
     SSD_DTYPE_BF16, SSD_DTYPE_F32, SSD_FLAG_GENERIC_KERNELS, SSD_FLAG_UNFUSED, SSD_FLAG_PER_SEQUENCE,
     SSD_OK,

@@ -47,6 +47,12 @@ class WorkspaceLayout(ctypes.Structure):
                 ("chain_sync_words", ctypes.c_int64)]
 
 
+class ScanProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
 MAX_STAGES = 8
 
 
@@ -64,7 +70,8 @@ class StageTimes(ctypes.Structure):
 
 
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-            "ssd_forward", "ssd_forward_timed", "ssd_step", "ssd_get_workspace_layout",
+            "ssd_forward", "ssd_forward_timed", "ssd_step", "ssd_selective_scan",
+            "ssd_get_workspace_layout",
             "ssd_status_string", "ssd_last_error_detail")
 
 _lock = threading.Lock()
@@ -92,8 +99,10 @@ def load(path: str = LIB_PATH):
         lib.ssd_forward_timed.argtypes = ([P] + [vp] * 11 + [ctypes.c_size_t, vp, ctypes.c_int32,
                                           ctypes.POINTER(StageTimes)])
         lib.ssd_step.argtypes = [P] + [vp] * 9
+        lib.ssd_selective_scan.argtypes = [ctypes.POINTER(ScanProblem)] + [vp] * 10
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step"):
+                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step",
+                  "ssd_selective_scan"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -305,3 +314,49 @@ def step(x, dt, A, B, C, D=None, state=None, *, y=None, stream=None):
                            _ptr(D), _ptr(state), _ptr(y), ctypes.c_void_p(stream.cuda_stream)),
            "ssd_step")
     return y
+
+
+def selective_scan(x, delta, A, B, C, D=None, initial_state=None, *, want_final_state=True,
+                   y=None, final_state=None, stream=None):
+    """The Mamba-1 selective scan (ssd_selective_scan): returns (y, final_state).
+
+    Shapes: x, delta (batch, L, dim); A (dim, N) fp32; B, C (batch, L, N);
+    D (dim,) fp32 or None; initial_state (batch, dim, N) fp32 or None. x,
+    delta, B, C share the dtype (bfloat16 or float32); dim must be a multiple
+    of 64 and N one of 16, 32, 64, 128, 256.
+    """
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, seqlen, dim)")
+    batch, L, Dm = x.shape
+    if A.dim() != 2 or A.shape[0] != Dm or A.dtype != torch.float32:
+        raise ValueError("A must be (dim, dstate) float32")
+    N = A.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU (got %s)" % dev)
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be bfloat16 or float32")
+    for name, t, shape in (("delta", delta, (batch, L, Dm)), ("B", B, (batch, L, N)),
+                           ("C", C, (batch, L, N))):
+        if tuple(t.shape) != shape or t.dtype != x.dtype or t.device != dev:
+            raise ValueError("%s must be %s %s on %s" % (name, shape, x.dtype, dev))
+    if D is not None and (tuple(D.shape) != (Dm,) or D.dtype != torch.float32):
+        raise ValueError("D must be (dim,) float32")
+    if initial_state is not None and (tuple(initial_state.shape) != (batch, Dm, N)
+                                      or initial_state.dtype != torch.float32):
+        raise ValueError("initial_state must be (%d, %d, %d) float32" % (batch, Dm, N))
+    prob = ScanProblem(batch, L, Dm, N, _DTYPES[x.dtype], 0)
+    x, delta, A, B, C = (t.contiguous() for t in (x, delta, A, B, C))
+    D = D.contiguous() if D is not None else None
+    h0 = initial_state.contiguous() if initial_state is not None else None
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((batch, Dm, N), device=dev, dtype=torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(load().ssd_selective_scan(ctypes.byref(prob), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
+                                     _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(final_state),
+                                     ctypes.c_void_p(stream.cuda_stream)),
+           "ssd_selective_scan")
+    return y, final_state

@@ -29,6 +29,7 @@
 #include "ssd.h"
 #include "ssd_internal.h"
 #include "step.h"
+#include "scan.h"
 
 namespace {
 
@@ -494,6 +495,51 @@ ssd_status ssd_step(const ssd_problem *p, const void *x, const void *dt, const f
   if (ssd::launch_step(a, p->dtype == SSD_DTYPE_BF16, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return fail(SSD_ERR_HIP, "step kernel launch failed");
+  return SSD_OK;
+}
+
+ssd_status ssd_selective_scan(const ssd_scan_problem *p, const void *x, const void *delta,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const float *initial_state, void *y, float *final_state,
+                              void *stream) {
+  g_detail.clear();
+  if (!p) return fail(SSD_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 0 || p->seqlen < 0 || p->dim < 1)
+    return fail(SSD_ERR_INVALID_ARG, "sizes must be valid (batch %d >= 0, seqlen %d >= 0, dim %d >= 1)",
+                p->batch, p->seqlen, p->dim);
+  if (p->flags != 0) return fail(SSD_ERR_INVALID_ARG, "the scan takes no flags (0x%x)", p->flags);
+  if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+  if (p->dstate != 16 && p->dstate != 32 && p->dstate != 64 && p->dstate != 128 &&
+      p->dstate != 256)
+    return fail(SSD_ERR_UNSUPPORTED, "dstate %d not in {16, 32, 64, 128, 256}", p->dstate);
+  if (p->dim % 64 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "dim %d is not a multiple of 64", p->dim);
+  if (p->batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d above 65535", p->batch);
+  if (p->batch == 0) return SSD_OK;
+  const bool tokens = p->seqlen > 0;
+  if (!A || (tokens && (!x || !delta || !B || !C || !y)))
+    return fail(SSD_ERR_INVALID_ARG, "A, and with tokens x, delta, B, C and y, must be non-NULL");
+  if (!aligned16(x) || !aligned16(delta) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+      !aligned16(A) || !aligned16(initial_state) || !aligned16(final_state))
+    return fail(SSD_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  ssd::ScanArgs a{};
+  a.x = x;
+  a.delta = delta;
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.D = D;
+  a.h0 = initial_state;
+  a.y = y;
+  a.hT = final_state;
+  a.batch = p->batch;
+  a.L = p->seqlen;
+  a.dim = p->dim;
+  a.N = p->dstate;
+  if (ssd::launch_selective_scan(a, p->dtype == SSD_DTYPE_BF16, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return fail(SSD_ERR_HIP, "selective scan kernel launch failed");
   return SSD_OK;
 }
 

@@ -193,3 +193,31 @@ def make_step_inputs(batch: int, nheads: int, headdim: int, dstate: int, ngroups
                 B=_cast(B, dtype), C=_cast(C, dtype),
                 D=torch.from_numpy(D.astype(np.float32)),
                 state=torch.from_numpy(state))
+
+
+def make_scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str, seed: int,
+                     h0_std: float = 0.0) -> dict:
+    """Seeded inputs of the Mamba-1 selective scan, with the value recipe of
+    the workloads above: x, B, C, D ~ N(0, 1); delta = softplus(z - 2);
+    A[d, n] = -exp(U(0, 2)), one rate per channel and state index; an
+    optional fp32 initial state ~ N(0, h0_std^2).
+
+    Draw order: x, B, C, z, u (for A), D, h0. Returns x, delta (batch, L, dim)
+    and B, C (batch, L, dstate) in ``dtype``; A (dim, dstate), D (dim,) and
+    h0 (batch, dim, dstate) or None in fp32.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
+    B = rng.standard_normal((batch, seqlen, dstate), dtype=np.float32)
+    C = rng.standard_normal((batch, seqlen, dstate), dtype=np.float32)
+    z = rng.standard_normal((batch, seqlen, dim), dtype=np.float32)
+    u = rng.uniform(0.0, 2.0, size=(dim, dstate))
+    D = rng.standard_normal(dim)
+    h0 = None
+    if h0_std > 0:
+        h0 = torch.from_numpy(rng.standard_normal((batch, dim, dstate), dtype=np.float32)
+                              * np.float32(h0_std))
+    return dict(x=_cast(x, dtype), delta=_cast(_softplus(z - 2.0), dtype),
+                A=torch.from_numpy((-np.exp(u)).astype(np.float32)),
+                B=_cast(B, dtype), C=_cast(C, dtype),
+                D=torch.from_numpy(D.astype(np.float32)), h0=h0)

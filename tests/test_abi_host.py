@@ -202,3 +202,51 @@ def test_step_rejects_null_and_misaligned_pointers(lib):
         ptrs[i] = vp(4096 * (i + 1) + 8)
         assert _step_status(lib, prob, ptrs) == ssd.SSD_ERR_INVALID_ARG, i
     assert "aligned" in lib.ssd_last_error_detail().decode()
+
+
+def _scan_status(lib, prob, ptrs=None):
+    """ssd_selective_scan's status for pointer values that are never
+    dereferenced: each case is rejected (or empty) before anything is enqueued."""
+    vp = ctypes.c_void_p
+    if ptrs is None:
+        ptrs = [vp(4096 * (i + 1)) for i in range(9)]
+    return lib.ssd_selective_scan(ctypes.byref(prob), *ptrs, vp(None))
+
+
+def SP(**kw):
+    base = dict(batch=2, seqlen=100, dim=128, dstate=16, dtype=ssd.SSD_DTYPE_BF16, flags=0)
+    base.update(kw)
+    return ssd.ScanProblem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"batch": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"seqlen": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"dim": 0}, ssd.SSD_ERR_INVALID_ARG),
+    ({"flags": 1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"dtype": 5}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 24}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 512}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dim": 96}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"batch": 70000}, ssd.SSD_ERR_UNSUPPORTED),
+])
+def test_scan_validate(lib, kw, status):
+    assert _scan_status(lib, SP(**kw)) == status
+
+
+def test_scan_empty_batch_is_a_no_op(lib):
+    assert _scan_status(lib, SP(batch=0), [ctypes.c_void_p(None)] * 9) == ssd.SSD_OK
+
+
+def test_scan_rejects_null_and_misaligned_pointers(lib):
+    vp = ctypes.c_void_p
+    good = [vp(4096 * (i + 1)) for i in range(9)]
+    # x, delta, A, B, C, y are required when there are tokens (D, h0, hT optional)
+    for i in (0, 1, 2, 3, 4, 7):
+        ptrs = list(good)
+        ptrs[i] = vp(None)
+        assert _scan_status(lib, SP(), ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    for i in (0, 1, 2, 3, 4, 6, 7, 8):
+        ptrs = list(good)
+        ptrs[i] = vp(4096 * (i + 1) + 4)
+        assert _scan_status(lib, SP(), ptrs) == ssd.SSD_ERR_INVALID_ARG, i
