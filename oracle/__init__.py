@@ -216,3 +216,20 @@ def chunk_log_decay(dt, A, seq_lens, Q: int):
             block[:, :n] = np.cumsum(dt[a + c0:a + c0 + n] * A[None, :], axis=0).T
             out.append(block)
     return np.stack(out) if out else np.zeros((0, H, Q))
+
+
+def dt_softplus(dt_raw, dt_bias=None):
+    """The step as the recurrence uses it when the caller passes the step's
+    pre-activation: softplus(dt_raw + dt_bias[h]), in fp64.
+
+    The selection mechanism makes the step a function of the input and passes
+    it through the softplus activation (tj-hxxt.cn long read of the Mamba-1
+    paper, part III (二), the step's activation tau_delta); dt_bias is the
+    learned per-head offset added before it. dt_raw (..., H) in any float
+    dtype, dt_bias (H,) or None. softplus(v) = log(1 + e^v), evaluated as
+    logaddexp(0, v) so that large v does not overflow.
+    """
+    v = _np(dt_raw)
+    if dt_bias is not None:
+        v = v + _np(dt_bias)
+    return np.logaddexp(0.0, v)
