@@ -154,6 +154,21 @@ ssd_status ssd_forward(const ssd_problem *prob, const void *x, const void *dt,
                        const int32_t *cu_seqlens, void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* ssd_forward with the step activation fused in: dt_raw holds the step's
+ * pre-activation and every kernel uses
+ *   dt[t, h] = softplus(dt_raw[t, h] + dt_bias[h]),  softplus(v) = log(1 + e^v)
+ * in fp32 (not rounded to the dtype), which is how the selection mechanism
+ * produces the step (tj-hxxt.cn long read of the Mamba-1 paper, part III (2):
+ * the step passes through the softplus activation tau_delta). dt_bias is
+ * (H) fp32 on the device, NULL = no offset; there is no clamp. Every other
+ * argument, the layouts, the workspace and the errors are those of
+ * ssd_forward. */
+ssd_status ssd_forward_dt_softplus(const ssd_problem *prob, const void *x, const void *dt_raw,
+                                   const float *dt_bias, const float *A, const void *B,
+                                   const void *C, const float *D, const float *initial_state,
+                                   const int32_t *cu_seqlens, void *y, float *final_state,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Per-kernel timing of the same launch sequence (a measurement aid).
  * Runs `iterations` back-to-back forward passes exactly as ssd_forward would
  * enqueue them, with a HIP event recorded before the first kernel and after

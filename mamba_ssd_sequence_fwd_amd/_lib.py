@@ -70,7 +70,8 @@ class StageTimes(ctypes.Structure):
 
 
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-            "ssd_forward", "ssd_forward_timed", "ssd_step", "ssd_selective_scan",
+            "ssd_forward", "ssd_forward_dt_softplus", "ssd_forward_timed", "ssd_step",
+            "ssd_selective_scan",
             "ssd_get_workspace_layout",
             "ssd_status_string", "ssd_last_error_detail")
 
@@ -99,10 +100,11 @@ def load(path: str = LIB_PATH):
         lib.ssd_forward_timed.argtypes = ([P] + [vp] * 11 + [ctypes.c_size_t, vp, ctypes.c_int32,
                                           ctypes.POINTER(StageTimes)])
         lib.ssd_step.argtypes = [P] + [vp] * 9
+        lib.ssd_forward_dt_softplus.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
         lib.ssd_selective_scan.argtypes = [ctypes.POINTER(ScanProblem)] + [vp] * 10
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
                   "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step",
-                  "ssd_selective_scan"):
+                  "ssd_selective_scan", "ssd_forward_dt_softplus"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
         lib.ssd_status_string.restype = ctypes.c_char_p
@@ -168,11 +170,16 @@ class Plan:
     (batch, L, G, N); D (H,) fp32 or None; initial_state (batch | num_seqs,
     H, P, N) fp32 or None; cu_seqlens (num_seqs + 1,) int32 (CPU or GPU) or
     None. x, dt, B, C share the dtype (bfloat16 or float32).
+
+    With ``dt_softplus=True`` dt holds the step's pre-activation and the
+    kernels use softplus(dt + dt_bias[h]) (ssd_forward_dt_softplus); dt_bias
+    is (H,) fp32 or None.
     """
 
     def __init__(self, x, dt, A, B, C, D=None, initial_state=None, chunk_size=256,
                  cu_seqlens=None, *, want_final_state=True, generic=False,
-                 unfused=False, per_sequence=False, check_cu_seqlens=True):
+                 unfused=False, per_sequence=False, check_cu_seqlens=True,
+                 dt_softplus=False, dt_bias=None):
         if x.dim() != 4:
             raise ValueError("x must be (batch, seqlen, nheads, headdim)")
         batch, L, H, P = x.shape
@@ -211,6 +218,14 @@ class Plan:
             if check_cu_seqlens or cu_seqlens.device.type == "cpu":
                 validate_cu_seqlens(self.prob, cu_seqlens.detach().cpu())
             cu_dev = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        if dt_bias is not None:
+            if not dt_softplus:
+                raise ValueError("dt_bias needs dt_softplus=True")
+            if tuple(dt_bias.shape) != (H,) or dt_bias.dtype != torch.float32 or dt_bias.device != dev:
+                raise ValueError("dt_bias must be (H,) float32 on %s" % dev)
+            dt_bias = dt_bias.contiguous()
+        self.dt_softplus = bool(dt_softplus)
+        self.dt_bias = dt_bias
         self.inputs = [t.contiguous() if t is not None else None
                        for t in (x, dt, A, B, C, D, initial_state)]
         self.cu = cu_dev
@@ -226,6 +241,14 @@ class Plan:
         if stream is None:
             stream = torch.cuda.current_stream(self.y.device)
         x, dt, A, B, C, D, h0 = self.inputs
+        if self.dt_softplus:
+            _check(load().ssd_forward_dt_softplus(
+                ctypes.byref(self.prob), _ptr(x), _ptr(dt), _ptr(self.dt_bias), _ptr(A),
+                _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(self.cu), _ptr(self.y),
+                _ptr(self.final_state), _ptr(self.workspace),
+                ctypes.c_size_t(self.workspace.numel()), ctypes.c_void_p(stream.cuda_stream)),
+                "ssd_forward_dt_softplus")
+            return self.y, self.final_state
         _check(load().ssd_forward(
             ctypes.byref(self.prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
             _ptr(D), _ptr(h0), _ptr(self.cu), _ptr(self.y), _ptr(self.final_state),
@@ -236,6 +259,8 @@ class Plan:
     def run_timed(self, iterations: int, stream=None) -> StageTimes:
         """``iterations`` passes with a HIP event after every kernel; waits for
         them and returns the per-kernel times (see ssd_forward_timed)."""
+        if self.dt_softplus:
+            raise ValueError("run_timed times ssd_forward; it has no raw-step variant")
         if stream is None:
             stream = torch.cuda.current_stream(self.y.device)
         x, dt, A, B, C, D, h0 = self.inputs

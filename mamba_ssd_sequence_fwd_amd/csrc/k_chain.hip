@@ -349,7 +349,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   float dtv;
   {
     const int t = min(tid, k.len - 1);
-    const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
+    const float d = dt_of(a, (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h], h);
     dtv = tid < k.len ? d : 0.f;  // zero past the chunk end (and for tid >= Q)
   }
   const int pair = k.seq * a.H + h;

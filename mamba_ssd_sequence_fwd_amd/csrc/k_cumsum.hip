@@ -33,7 +33,8 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(Args a) {
     float v[kCsHeads];
 #pragma unroll
     for (int j = 0; j < kCsHeads; ++j)  // unconditional loads (clamped), then select
-      v[j] = ld<T>(a.dt, (size_t)(k.start + lc) * a.H + h0 + min(j, nh - 1));
+      v[j] = dt_of(a, ld<T>(a.dt, (size_t)(k.start + lc) * a.H + h0 + min(j, nh - 1)),
+                   h0 + min(j, nh - 1));
 #pragma unroll
     for (int j = 0; j < kCsHeads; ++j) v[j] = (l < k.len) ? v[j] : 0.f;
 #pragma unroll

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (c0 < c1) {
     chunk_of(a, c0, k);
     const int t = min(tid, k.len - 1);
-    const float d = (float)dtg[(size_t)(k.start + t) * a.H];
+    const float d = dt_of(a, (float)dtg[(size_t)(k.start + t) * a.H], h);
     dtv = tid < k.len ? d : 0.f;
     async_tile<N, Q>(sB, bg + (size_t)k.start * ldb, ldb, k.len, zeros);
     async_tile<kP, Q>(sX[0], xg + (size_t)k.start * ldx, ldx, k.len, zeros);
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (c + 1 < c1) {
       chunk_of(a, c + 1, k);
       const int t = min(tid, k.len - 1);
-      const float d = (float)dtg[(size_t)(k.start + t) * a.H];
+      const float d = dt_of(a, (float)dtg[(size_t)(k.start + t) * a.H], h);
       dtv = tid < k.len ? d : 0.f;
       async_tile<N, Q>(sB, bg + (size_t)k.start * ldb, ldb, k.len, zeros);
       async_tile<kP, Q>(sX[cur ^ 1], xg + (size_t)k.start * ldx, ldx, k.len, zeros);

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k_chunk_state_generic(Args a) {
   const float *cs = a.cs + ((size_t)c * a.H + h) * a.Q;
   const float last = cs[k.len - 1];
   for (int l = tid; l < k.len; l += 256)
-    s_w[l] = exp2_fast(last - cs[l]) * ld<T>(a.dt, (size_t)(k.start + l) * a.H + h);
+    s_w[l] = exp2_fast(last - cs[l]) * dt_of(a, ld<T>(a.dt, (size_t)(k.start + l) * a.H + h), h);
   __syncthreads();
   float acc = 0.f;
   for (int l0 = 0; l0 < k.len; l0 += 32) {
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Args a) {
   const float *cs = a.cs + ((size_t)c * a.H + h) * a.Q;
   for (int i = tid; i < k.len; i += 256) {
     s_cs[i] = cs[i];
-    s_dt[i] = ld<T>(a.dt, (size_t)(k.start + i) * a.H + h);
+    s_dt[i] = dt_of(a, ld<T>(a.dt, (size_t)(k.start + i) * a.H + h), h);
   }
   for (int e = tid; e < kScanRows * N; e += 256) {
     const int rr = e / N, n = e - rr * N;

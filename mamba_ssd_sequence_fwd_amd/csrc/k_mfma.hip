@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
     if (Q >= 256 || l < Q) {
       const int lc = min(l, k.len - 1);
       const float w = exp2_fast(last - cs[lc]) *
-                      (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h];
+                      dt_of(a, (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h], h);
       sW[l] = l < k.len ? w : 0.f;
     }
   }
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_mfma(Args a, const bf16 *cb) {
   const int lc = min(tid, k.len - 1);  // one token per thread (NTHR == Q)
   const float cst = cs[lc];
   const float cse = cs[min(tid | 31, k.len - 1)];
-  const float d = (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h];
+  const float d = dt_of(a, (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h], h);
   const float dtv = tid < k.len ? d : 0.f;
   sCs[tid] = cst;
   sDt[tid] = dtv;

@@ -394,6 +394,23 @@ ssd_status ssd_forward(const ssd_problem *p, const void *x, const void *dt,
   return enqueue(a, L, p->dtype == SSD_DTYPE_BF16, s, nullptr);
 }
 
+ssd_status ssd_forward_dt_softplus(const ssd_problem *p, const void *x, const void *dt_raw,
+                                   const float *dt_bias, const float *A, const void *B,
+                                   const void *C, const float *D, const float *initial_state,
+                                   const int32_t *cu_seqlens, void *y, float *final_state,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  ssd_status st = check_args(p, x, dt_raw, A, B, C, cu_seqlens, y, initial_state, final_state,
+                             workspace, workspace_bytes);
+  if (st != SSD_OK) return st;
+  const Layout L = make_layout(*p);
+  ssd::Args a = make_args(p, L, x, dt_raw, A, B, C, D, initial_state, cu_seqlens, y,
+                          final_state, workspace);
+  a.dt_softplus = 1;
+  a.dt_bias = dt_bias;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return enqueue(a, L, p->dtype == SSD_DTYPE_BF16, s, nullptr);
+}
+
 ssd_status ssd_forward_timed(const ssd_problem *p, const void *x, const void *dt,
                              const float *A, const void *B, const void *C, const float *D,
                              const float *initial_state, const int32_t *cu_seqlens,

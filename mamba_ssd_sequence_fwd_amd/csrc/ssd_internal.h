@@ -40,6 +40,8 @@ struct Args {
   int32_t heads_per_group;
   int32_t rec_off;      // int offset of the chunk records inside plan
   int32_t order_off;    // int offset of the chunk order (by index in sequence) inside plan
+  const float *dt_bias; // (H) or null: per-head offset of the step pre-activation
+  int32_t dt_softplus;  // 0: dt is the step; 1: dt is its pre-activation
 };
 
 // Ints ahead of the per-(sequence, head) counters in Args::sync.
@@ -110,6 +112,16 @@ __device__ __forceinline__ float ld(const void *p, size_t i) {
 // 2^x on the hardware exp unit (v_exp_f32); exact 0 for very negative x.
 __device__ __forceinline__ float exp2_fast(float x) {
   return __builtin_amdgcn_exp2f(x);
+}
+
+// The step of token t, head h, as the recurrence uses it: dt as given, or,
+// when dt holds the step's pre-activation, softplus(dt + dt_bias[h]) (the
+// selection mechanism's step activation). softplus(v) = log(1 + e^v), taken
+// as v itself above 20 (the difference is below fp32 resolution).
+__device__ __forceinline__ float dt_of(const Args &a, float raw, int h) {
+  if (!a.dt_softplus) return raw;
+  const float v = raw + (a.dt_bias ? a.dt_bias[h] : 0.f);
+  return v > 20.f ? v : log1pf(__expf(v));
 }
 
 // ---- wavefront (64-lane) primitives ---------------------------------------
