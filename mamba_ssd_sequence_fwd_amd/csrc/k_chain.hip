@@ -55,6 +55,7 @@ namespace ssd {
 
 constexpr float kLog2eChain = 1.4426950408889634f;
 constexpr int kChainWaves = 4;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Intra-chunk outputs of the 32-row tile i (rows 32i .. 32i+31), both 16-row
 // halves u, added into Y[u] (transposed: lane holds column l = 32i + 16u +
@@ -221,7 +222,13 @@ __device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int le
       const auto sx = __builtin_amdgcn_permlane16_swap(pk[2 * m][0], pk[2 * m + 1][0], false, false);
       const auto sy = __builtin_amdgcn_permlane16_swap(pk[2 * m][1], pk[2 * m + 1][1], false, false);
       const uint4 o = make_uint4(sx[0], sy[0], sx[1], sy[1]);
-      if (l < len) *reinterpret_cast<uint4 *>(yr + 32 * m) = o;
+      // y is written once and read by nothing in this pass: nontemporal
+      // stores (measured 5-8% faster on the 2.7B-shaped workload, 2%
+      // slower on the long varlen one)
+      if (l < len) {
+        const u32x4_t ov = {o.x, o.y, o.z, o.w};
+        __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t *>(yr + 32 * m));
+      }
     }
   }
 }
