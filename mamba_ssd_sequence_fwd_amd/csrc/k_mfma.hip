@@ -34,8 +34,12 @@ namespace ssd {
 // One workgroup (4 waves) per (chunk, head); wave w owns n in
 // [w*N/4, (w+1)*N/4) and all 64 p. Tokens go through LDS 128 at a time.
 // ============================================================================
+// Three workgroups per CU fit the LDS for N <= 128; the occupancy request keeps
+// the register allocation within that (156 VGPRs for N = 128, Q = 256, where
+// the compiler otherwise takes 176 and runs two waves per SIMD).
 template <int N, int Q>
-__global__ __launch_bounds__(256) void k_chunk_state_mfma(Args a) {
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(N == 256 ? 2 : 3))) void k_chunk_state_mfma(Args a) {
   constexpr int QH = Q < 128 ? Q : 128;
   constexpr int NT = N / 64;  // 16-wide n tiles per wave
   __shared__ __attribute__((aligned(16))) bf16 sX[kP * QH];
