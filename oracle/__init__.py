@@ -16,9 +16,11 @@ Two independent formulations of the same linear map:
   matrix, equivalently a masked attention whose mask is that matrix).
 
 A third module, :mod:`oracle.step`, is the decode step (one token of the
-recurrence per sequence, the state carried by the caller), and a fourth,
+recurrence per sequence, the state carried by the caller), a fourth,
 :mod:`oracle.selective_scan`, the Mamba-1 selective scan (a diagonal A per
-channel) that the SSD layer is compared with, both in numpy.
+channel) that the SSD layer is compared with, and a fifth, :mod:`oracle.conv`,
+the causal depthwise convolution and activation that produce the layer's x,
+B and C, all in numpy.
 
 Every function here is plain and slow on purpose.
 """

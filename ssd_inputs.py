@@ -221,3 +221,44 @@ def make_scan_inputs(batch: int, seqlen: int, dim: int, dstate: int, dtype: str,
                 A=torch.from_numpy((-np.exp(u)).astype(np.float32)),
                 B=_cast(B, dtype), C=_cast(C, dtype),
                 D=torch.from_numpy(D.astype(np.float32)), h0=h0)
+
+
+def make_conv_inputs(batch: int, seqlen: int, x_dim: int, bc_dim: int, width: int, dtype: str,
+                     seed: int, seq_lens=None, history: bool = False, pad_cols: int = 0,
+                     lead_cols: int = 0) -> dict:
+    """Seeded inputs of the convolution front (packed x, B, C channels).
+
+    Dense (``seq_lens`` None): ``batch`` rows of ``seqlen`` tokens. Packed
+    (``seq_lens`` a list, batch 1): those lengths back to back, with
+    cu_seqlens. The packed input rows are ``lead_cols + channels + pad_cols``
+    wide and the channels start at ``lead_cols``, as when xBC is a slice of a
+    wider projection output (``xbc`` is that slice, ``xbc_full`` the whole).
+
+    Value recipe: inputs ~ N(0, 1); weight and bias ~ U(-1/sqrt(K),
+    1/sqrt(K)), the usual fan-in bound of a K-tap filter; optional history
+    ~ N(0, 1). Draw order: the full input rows, weight, bias, history.
+    Inputs and history are rounded once to ``dtype``; weight and bias stay
+    float32.
+    """
+    rng = np.random.default_rng(seed)
+    ch = x_dim + 2 * bc_dim
+    cu = None
+    if seq_lens is not None:
+        lens = [int(v) for v in seq_lens]
+        T, nseq = int(sum(lens)), len(lens)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    else:
+        T, nseq = batch * seqlen, batch
+    full = rng.standard_normal((T, lead_cols + ch + pad_cols), dtype=np.float32)
+    bound = 1.0 / np.sqrt(width)
+    w = rng.uniform(-bound, bound, size=(ch, width)).astype(np.float32)
+    b = rng.uniform(-bound, bound, size=ch).astype(np.float32)
+    hist = None
+    if history:
+        hist = _cast(rng.standard_normal((nseq, width - 1, ch), dtype=np.float32), dtype)
+    xbc_full = _cast(full, dtype)
+    return dict(xbc_full=xbc_full, xbc=xbc_full[:, lead_cols:lead_cols + ch],
+                weight=torch.from_numpy(w), bias=torch.from_numpy(b), history=hist,
+                cu_seqlens=cu, num_seqs=0 if seq_lens is None else nseq, T=T,
+                batch=batch if seq_lens is None else 1,
+                seqlen=seqlen if seq_lens is None else T)
