@@ -88,6 +88,8 @@ TRAFFIC_PROFILES = {
                                  ("k_chain.hip", "mfma_common.h", "ssd_internal.h")),
     ("ssd_step", "decode-2.7b-b256"): ("ssd_step_decode-2.7b-b256.md",
                                        ("k_step.hip", "step.h", "ssd_internal.h")),
+    ("ssd_conv", "conv-front-2.7b"): ("ssd_conv_front-2.7b.md",
+                                      ("k_conv.hip", "conv.h", "ssd_internal.h")),
 }
 
 
@@ -158,6 +160,46 @@ def cpu_baseline(inp: dict, w: si.Workload, budget_s: float, threads: int = 0) -
                           done, w.name, len(order), done / len(order), elapsed, threads)}
 
 
+def evict_caches(buf):
+    """Read ``buf`` (COLD_EVICT_BYTES, twice the MALL) so that the L2s and the
+    MALL hold its clean lines and none of the timed kernel's data. A write
+    would leave dirty lines whose write-back the next kernel would pay for."""
+    return torch.sum(buf)
+
+
+def time_launches(run, args, stream):
+    """Time ``args.steps`` calls of ``run`` with HIP events on ``stream``:
+    back to back (warm caches), or with ``args.cold`` each call after
+    evict_caches. ``args.warmup``
+    untimed calls first. Returns (ms per call, wall seconds of the timed
+    region)."""
+    for _ in range(args.warmup):
+        run()
+    dev = torch.device("cuda:0")
+    evict = torch.zeros(COLD_EVICT_BYTES // 4, device=dev) if args.cold else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    total_ms = 0.0
+    if not args.cold:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        e1.synchronize()
+        total_ms = e0.elapsed_time(e1)
+    else:
+        for i in range(args.steps):
+            evict_caches(evict)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            e1.synchronize()
+            total_ms += e0.elapsed_time(e1)
+    return total_ms / args.steps, time.perf_counter() - t0
+
+
 def bench_decode(args):
     """Decode step: K back-to-back ssd_step calls on one state buffer (each
     sequence advances one token per call), timed with HIP events on the
@@ -170,31 +212,8 @@ def bench_decode(args):
     A, D, state = inp["A"].to(dev), inp["D"].to(dev), inp["state"].to(dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream)
-    evict = torch.empty(COLD_EVICT_BYTES // 4, device=dev) if args.cold else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    total_ms = 0.0
-    if not args.cold:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream)
-        e1.record(stream)
-        e1.synchronize()
-        total_ms = e0.elapsed_time(e1)
-    else:
-        for i in range(args.steps):
-            evict.fill_(float(i))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream)
-            e1.record(stream)
-            e1.synchronize()
-            total_ms += e0.elapsed_time(e1)
-    wall = time.perf_counter() - t0
-    ms = total_ms / args.steps
+    ms, wall = time_launches(lambda: ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream),
+                             args, stream)
     e = 2
     alg_bytes = batch * H * P * N * 4 * 2 + batch * (2 * H * P * e + H * e + 2 * G * N * e)
     alg_flops = batch * H * P * N * 6
@@ -238,31 +257,7 @@ def bench_scan(args):
     stream = torch.cuda.current_stream(dev)
     run = lambda: ssd.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["h0"],
                                      y=y, final_state=hT, stream=stream)
-    for _ in range(args.warmup):
-        run()
-    evict = torch.empty(COLD_EVICT_BYTES // 4, device=dev) if args.cold else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    total_ms = 0.0
-    if not args.cold:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            run()
-        e1.record(stream)
-        e1.synchronize()
-        total_ms = e0.elapsed_time(e1)
-    else:
-        for i in range(args.steps):
-            evict.fill_(float(i))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            run()
-            e1.record(stream)
-            e1.synchronize()
-            total_ms += e0.elapsed_time(e1)
-    wall = time.perf_counter() - t0
-    ms = total_ms / args.steps
+    ms, wall = time_launches(run, args, stream)
     elems = batch * L * Dm * N
     alg_bytes = batch * L * (3 * Dm * 2 + 2 * N * 2) + Dm * N * 4 + 2 * batch * Dm * N * 4
     achieved = elems / (ms * 1e-3)
@@ -281,6 +276,49 @@ def bench_scan(args):
         "kernels": {"selective_scan": {"ms": round(ms, 5), "alg_bytes": alg_bytes,
                                        "GB/s": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
                                        "elements": elems}},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_conv(args):
+    """Convolution front at the 2.7B shapes: batch 8, 2048 tokens, x 5120
+    channels (80 heads x 64), B and C 128 channels each, 4 taps, bf16, with
+    the history read and written; K back-to-back launches timed with HIP
+    events on the kernel's stream. Every input is read once and every output
+    written once, so HBM bandwidth bounds it."""
+    batch, L, x_dim, bc_dim, K = 8, 2048, 5120, 128, 4
+    ch = x_dim + 2 * bc_dim
+    inp = si.make_conv_inputs(batch, L, x_dim, bc_dim, K, "bf16", seed=4300, history=True)
+    dev = torch.device("cuda:0")
+    xbc = inp["xbc"].view(batch, L, ch).to(dev)
+    w, b, hist = inp["weight"].to(dev), inp["bias"].to(dev), inp["history"].to(dev)
+    x = torch.empty((batch, L, x_dim), device=dev, dtype=torch.bfloat16)
+    B = torch.empty((batch, L, bc_dim), device=dev, dtype=torch.bfloat16)
+    C = torch.empty_like(B)
+    ho = torch.empty_like(hist)
+    stream = torch.cuda.current_stream(dev)
+    ms, wall = time_launches(lambda: ssd.conv1d_silu(xbc, w, b, x_dim, bc_dim, hist, x=x, B=B,
+                                                     C=C, history_out=ho, stream=stream),
+                             args, stream)
+    T, e = batch * L, 2
+    alg_bytes = 2 * T * ch * e + 2 * batch * (K - 1) * ch * e + ch * (K + 1) * 4
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    workload = "conv-front-2.7b"
+    out = {
+        "metric": "SSD conv front tokens/s (causal depthwise conv1d + SiLU producing x, B, C)",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "batch": batch, "seq_len": L, "x_dim": x_dim,
+                   "bc_dim": bc_dim, "width": K, "channels": ch,
+                   "caches": "cold" if args.cold else "warm"},
+        "roofline": {"kernel": "ssd_conv", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("ssd_conv", workload)},
+        "kernels": {"ssd_conv": {"ms": round(ms, 5), "alg_bytes": alg_bytes,
+                                 "alg_flops": T * ch * (2 * K + 4), "GB/s": round(gbs, 1)}},
         "wall_s_timed_region": round(wall, 4),
     }
     print(json.dumps(out), flush=True)
@@ -307,9 +345,13 @@ def main():
                     help="instead of the SSD forward pass, time the Mamba-1 selective scan "
                          "(ssd_selective_scan) at the 2.7B shapes (batch 8, 2048 tokens, 5120 "
                          "channels) with state size N per channel")
+    ap.add_argument("--conv", action="store_true",
+                    help="instead of the SSD forward pass, time the convolution front "
+                         "(ssd_conv1d_silu) at the 2.7B shapes")
     ap.add_argument("--cold", action="store_true",
-                    help="before every timed pass, write a 512 MiB buffer so that the pass "
-                         "starts with the Infinity Cache (MALL) and the L2s holding none of its data")
+                    help="before every timed pass, read a 512 MiB buffer so that the pass "
+                         "starts with the Infinity Cache (MALL) and the L2s holding none of its "
+                         "data (and no dirty lines to write back)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy "
                          "of this many MiB (known HBM traffic) to calibrate byte counters")
@@ -340,6 +382,9 @@ def main():
     if args.scan:
         bench_scan(args)
         return
+    if args.conv:
+        bench_conv(args)
+        return
 
     w = si.CONFIGS[args.config]
     inp = si.make_inputs(w)
@@ -363,12 +408,12 @@ def main():
         per_kernel_ms = times.as_dict()
         total_ms = per_kernel_ms.pop("_total_ms")
     else:
-        # One pass at a time, each after an eviction write that the events
-        # do not cover; per-kernel and total times are summed over passes.
-        evict = torch.empty(COLD_EVICT_BYTES // 4, device=dev, dtype=torch.float32)
+        # One pass at a time, each after an eviction read that the events do
+        # not cover; per-kernel and total times are summed over passes.
+        evict = torch.zeros(COLD_EVICT_BYTES // 4, device=dev, dtype=torch.float32)
         per_kernel_ms, total_ms = {}, 0.0
         for i in range(args.steps):
-            evict.fill_(float(i))
+            evict_caches(evict)
             t = plan.run_timed(1, stream).as_dict()
             total_ms += t.pop("_total_ms")
             for k, v in t.items():

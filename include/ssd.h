@@ -300,6 +300,61 @@ ssd_status ssd_selective_scan(const ssd_scan_problem *prob, const void *x, const
                               const float *initial_state, void *y, float *final_state,
                               void *stream);
 
+/* The convolution front that produces the SSD layer's x, B and C: a causal
+ * depthwise 1-D convolution over the packed channels [x | B | C] of each
+ * token, followed by SiLU. In the Mamba-2 model one part of the input
+ * projection passes through a 1-D convolution that captures local
+ * dependencies without looking ahead (CSDN csdn_xmj page, related-article
+ * snippet on implementing the Mamba-2 model), and the Mamba block uses an
+ * activation where H3 had a gate (tj-hxxt.cn long read of the Mamba-1 paper,
+ * part III, the closing paragraph on the selection mechanism). With
+ * ch = x_dim + 2 bc_dim and K = width, per sequence and channel c, the K - 1
+ * inputs before the first token being the sequence's history rows (or zeros):
+ *   pre[t, c] = bias[c] + sum_{k < K} weight[c, k] * u[t - (K - 1) + k, c]
+ *   out[t, c] = pre[t, c] / (1 + exp(-pre[t, c]))
+ * (weight[c, K - 1] multiplies the current token). Channels [0, x_dim) of out
+ * go to x, the next bc_dim to B and the last bc_dim to C. Packed sequences
+ * never see each other's tokens. The history of a sequence is its last K - 1
+ * inputs, oldest first: history_out of one call is history_in of the next
+ * call over the same sequences (chunked prefill, then decode with seqlen 1).
+ *
+ * Problem: dense mode (num_seqs 0) has batch >= 0 rows of seqlen >= 0 tokens;
+ * packed mode (num_seqs > 0) has batch 1, seqlen = the total tokens and
+ * cu_seqlens. x_dim and bc_dim are multiples of 8 (x_dim = H * P and
+ * bc_dim = G * N for the SSD layer), ch >= 8; width in {2, 3, 4}; in_stride
+ * >= ch and a multiple of 16 bytes; dtype F32 or BF16; flags 0.
+ * Arguments (device pointers owned by the caller, 16-byte aligned where
+ * listed):
+ *   xbc          row t at xbc + t * in_stride, channels [0, ch)   dtype, aligned
+ *                (in_stride > ch reads a slice of a wider projection row)
+ *   weight       (ch, width) fp32 taps
+ *   bias         (ch) fp32, NULL = none
+ *   history_in   (batch | num_seqs, width - 1, ch) dtype, aligned, NULL = zeros
+ *   cu_seqlens   (num_seqs + 1) int32, packed mode only (NULL in dense mode):
+ *                0 = cu[0] <= cu[1] <= ... <= cu[num_seqs] = seqlen; zero
+ *                lengths allowed. Invalid device values never cause an
+ *                out-of-bounds access, but the outputs are then unspecified.
+ *   x            (tokens, x_dim) dtype (out), aligned
+ *   B, C         (tokens, bc_dim) dtype (out), aligned
+ *   history_out  (batch | num_seqs, width - 1, ch) dtype (out), aligned,
+ *                NULL = not written; must not overlap history_in
+ *   stream       a hipStream_t (NULL = the default stream)
+ * Arithmetic is fp32; bf16 outputs are rounded to nearest even; histories
+ * copy inputs exactly. Outputs must not overlap inputs. Errors:
+ * SSD_ERR_INVALID_ARG (malformed sizes, NULL or misaligned pointers),
+ * SSD_ERR_UNSUPPORTED (outside the set above), SSD_ERR_HIP; nothing is
+ * enqueued on error. No allocation, no workspace. */
+typedef struct ssd_conv_problem {
+  int32_t batch, seqlen, num_seqs;
+  int32_t x_dim, bc_dim, width, in_stride;
+  ssd_dtype dtype;
+  uint32_t flags;
+} ssd_conv_problem;
+ssd_status ssd_conv1d_silu(const ssd_conv_problem *prob, const void *xbc, const float *weight,
+                           const float *bias, const void *history_in,
+                           const int32_t *cu_seqlens, void *x, void *B, void *C,
+                           void *history_out, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

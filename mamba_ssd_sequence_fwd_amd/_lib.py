@@ -53,6 +53,14 @@ class ScanProblem(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class ConvProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("x_dim", ctypes.c_int32),
+                ("bc_dim", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("in_stride", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
 MAX_STAGES = 8
 
 
@@ -71,7 +79,7 @@ class StageTimes(ctypes.Structure):
 
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
             "ssd_forward", "ssd_forward_dt_softplus", "ssd_forward_timed", "ssd_step",
-            "ssd_selective_scan",
+            "ssd_selective_scan", "ssd_conv1d_silu",
             "ssd_get_workspace_layout",
             "ssd_status_string", "ssd_last_error_detail")
 
@@ -102,6 +110,7 @@ def load(path: str = LIB_PATH):
         lib.ssd_step.argtypes = [P] + [vp] * 9
         lib.ssd_forward_dt_softplus.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
         lib.ssd_selective_scan.argtypes = [ctypes.POINTER(ScanProblem)] + [vp] * 10
+        lib.ssd_conv1d_silu.argtypes = [ctypes.POINTER(ConvProblem)] + [vp] * 10
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
                   "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step",
                   "ssd_selective_scan", "ssd_forward_dt_softplus"):
@@ -385,3 +394,83 @@ def selective_scan(x, delta, A, B, C, D=None, initial_state=None, *, want_final_
                                      ctypes.c_void_p(stream.cuda_stream)),
            "ssd_selective_scan")
     return y, final_state
+
+
+def _check_offsets(cu, tokens: int):
+    """Host check of packed offsets: 0 = cu[0] <= ... <= cu[-1] = tokens."""
+    c = cu.detach().to("cpu", torch.int64)
+    if c.dim() != 1 or c.numel() < 2 or int(c[0]) != 0 or int(c[-1]) != tokens or \
+            bool((c[1:] < c[:-1]).any()):
+        raise ValueError("cu_seqlens must rise from 0 to the token count %d" % tokens)
+
+
+def conv1d_silu(xbc, weight, bias, x_dim, bc_dim, history=None, cu_seqlens=None, *,
+                want_history=True, x=None, B=None, C=None, history_out=None,
+                check_cu_seqlens=True, stream=None):
+    """The convolution front (ssd_conv1d_silu): causal depthwise conv1d over
+    the packed channels [x | B | C], then SiLU. Returns (x, B, C,
+    history_out).
+
+    xbc is (batch, L, ch) (dense) or (tokens, ch) with ``cu_seqlens``, ch =
+    x_dim + 2 * bc_dim, channels contiguous; its rows may be a slice of wider
+    rows (the row stride is passed through). weight (ch, K) and bias (ch,) are
+    float32; history (sequences, K - 1, ch) in xbc's dtype or None. Outputs
+    have xbc's leading shape with x_dim, bc_dim, bc_dim channels.
+    """
+    if xbc.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU (got %s)" % xbc.device)
+    if xbc.dtype not in _DTYPES:
+        raise ValueError("xbc must be bfloat16 or float32")
+    ch = x_dim + 2 * bc_dim
+    if xbc.shape[-1] != ch or xbc.stride(-1) != 1:
+        raise ValueError("xbc must end in %d contiguous channels" % ch)
+    dev = xbc.device
+    if cu_seqlens is not None:
+        if xbc.dim() != 2:
+            raise ValueError("packed xbc must be (tokens, channels)")
+        batch, L = 1, int(xbc.shape[0])
+        num_seqs = int(cu_seqlens.numel()) - 1
+        if check_cu_seqlens or cu_seqlens.device.type == "cpu":
+            _check_offsets(cu_seqlens, L)
+        cu_dev = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        nseq, lead = num_seqs, (L,)
+        in_stride = xbc.stride(0) if L > 1 else ch
+    else:
+        if xbc.dim() != 3:
+            raise ValueError("dense xbc must be (batch, seqlen, channels)")
+        batch, L = int(xbc.shape[0]), int(xbc.shape[1])
+        num_seqs, cu_dev, nseq, lead = 0, None, batch, (batch, L)
+        # token row t = b * L + l sits at b * stride(0) + l * stride(1)
+        if L > 1:
+            if batch > 1 and xbc.stride(0) != L * xbc.stride(1):
+                raise ValueError("the token rows of xbc must be evenly spaced")
+            in_stride = xbc.stride(1)
+        else:
+            in_stride = xbc.stride(0) if batch > 1 else ch
+    K = int(weight.shape[1]) if weight.dim() == 2 else 0
+    if tuple(weight.shape) != (ch, K) or weight.dtype != torch.float32:
+        raise ValueError("weight must be (%d, K) float32" % ch)
+    if bias is not None and (tuple(bias.shape) != (ch,) or bias.dtype != torch.float32):
+        raise ValueError("bias must be (%d,) float32" % ch)
+    hshape = (nseq, K - 1, ch)
+    if history is not None and (tuple(history.shape) != hshape or history.dtype != xbc.dtype):
+        raise ValueError("history must be %s %s" % (hshape, xbc.dtype))
+    weight = weight.contiguous()
+    bias = bias.contiguous() if bias is not None else None
+    history = history.contiguous() if history is not None else None
+    if x is None:
+        x = torch.empty(lead + (x_dim,), device=dev, dtype=xbc.dtype)
+    if B is None:
+        B = torch.empty(lead + (bc_dim,), device=dev, dtype=xbc.dtype)
+    if C is None:
+        C = torch.empty(lead + (bc_dim,), device=dev, dtype=xbc.dtype)
+    if history_out is None and want_history:
+        history_out = torch.empty(hshape, device=dev, dtype=xbc.dtype)
+    prob = ConvProblem(batch, L, num_seqs, x_dim, bc_dim, K, in_stride, _DTYPES[xbc.dtype], 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(load().ssd_conv1d_silu(ctypes.byref(prob), _ptr(xbc), _ptr(weight), _ptr(bias),
+                                  _ptr(history), _ptr(cu_dev), _ptr(x), _ptr(B), _ptr(C),
+                                  _ptr(history_out), ctypes.c_void_p(stream.cuda_stream)),
+           "ssd_conv1d_silu")
+    return x, B, C, history_out

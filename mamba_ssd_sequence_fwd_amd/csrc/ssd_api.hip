@@ -30,6 +30,7 @@
 #include "ssd_internal.h"
 #include "step.h"
 #include "scan.h"
+#include "conv.h"
 
 namespace {
 
@@ -557,6 +558,79 @@ ssd_status ssd_selective_scan(const ssd_scan_problem *p, const void *x, const vo
   if (ssd::launch_selective_scan(a, p->dtype == SSD_DTYPE_BF16, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return fail(SSD_ERR_HIP, "selective scan kernel launch failed");
+  return SSD_OK;
+}
+
+ssd_status ssd_conv1d_silu(const ssd_conv_problem *p, const void *xbc, const float *weight,
+                           const float *bias, const void *history_in,
+                           const int32_t *cu_seqlens, void *x, void *B, void *C,
+                           void *history_out, void *stream) {
+  g_detail.clear();
+  if (!p) return fail(SSD_ERR_INVALID_ARG, "problem is NULL");
+  if (p->batch < 0 || p->seqlen < 0 || p->num_seqs < 0 || p->x_dim < 0 || p->bc_dim < 0)
+    return fail(SSD_ERR_INVALID_ARG,
+                "sizes must be non-negative (batch %d, seqlen %d, num_seqs %d, x_dim %d, "
+                "bc_dim %d)", p->batch, p->seqlen, p->num_seqs, p->x_dim, p->bc_dim);
+  if (p->flags != 0)
+    return fail(SSD_ERR_INVALID_ARG, "the convolution takes no flags (0x%x)", p->flags);
+  if (p->dtype != SSD_DTYPE_F32 && p->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "dtype %d not supported", p->dtype);
+  if (p->width < 2 || p->width > 4)
+    return fail(SSD_ERR_UNSUPPORTED, "width %d not in {2, 3, 4}", p->width);
+  if (p->x_dim % 8 != 0 || p->bc_dim % 8 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "x_dim %d and bc_dim %d must be multiples of 8", p->x_dim,
+                p->bc_dim);
+  const int64_t ch = (int64_t)p->x_dim + 2 * (int64_t)p->bc_dim;
+  if (ch < 8 || ch > INT32_MAX / 8)
+    return fail(SSD_ERR_INVALID_ARG, "channel count %lld out of range",
+                (long long)ch);
+  const size_t esz = p->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  if (p->in_stride < ch || ((size_t)p->in_stride * esz) % 16 != 0)
+    return fail(SSD_ERR_INVALID_ARG,
+                "in_stride %d must be >= the channel count %lld and a multiple of 16 bytes",
+                p->in_stride, (long long)ch);
+  const bool varlen = p->num_seqs > 0;
+  if (varlen && p->batch != 1)
+    return fail(SSD_ERR_INVALID_ARG, "packed sequences take batch 1, got %d", p->batch);
+  if (varlen && !cu_seqlens)
+    return fail(SSD_ERR_INVALID_ARG, "num_seqs > 0 needs cu_seqlens");
+  const int64_t T = (int64_t)p->batch * p->seqlen;
+  const int64_t nseq = varlen ? p->num_seqs : p->batch;
+  const int64_t tiles = (T + ssd::kConvTile - 1) / ssd::kConvTile;
+  if (T > INT32_MAX - ssd::kConvTile ||
+      (tiles * (ch / 8) + ssd::kConvThreads - 1) / ssd::kConvThreads > INT32_MAX ||
+      (nseq * (ch / 8) + ssd::kConvThreads - 1) / ssd::kConvThreads > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "%lld tokens x %lld channels too large for one launch",
+                (long long)T, (long long)ch);
+  if (nseq == 0 || (T == 0 && !history_out)) return SSD_OK;
+  if (!weight) return fail(SSD_ERR_INVALID_ARG, "weight must be non-NULL");
+  if (T > 0 && (!xbc || (p->x_dim > 0 && !x) || (p->bc_dim > 0 && (!B || !C))))
+    return fail(SSD_ERR_INVALID_ARG, "xbc, and x, B, C for non-empty parts, must be non-NULL");
+  if (!aligned16(xbc) || !aligned16(x) || !aligned16(B) || !aligned16(C) ||
+      !aligned16(history_in) || !aligned16(history_out))
+    return fail(SSD_ERR_INVALID_ARG, "xbc, x, B, C and the histories must be 16-byte aligned");
+  ssd::ConvArgs a{};
+  a.xbc = xbc;
+  a.w = weight;
+  a.bias = bias;
+  a.hist_in = history_in;
+  a.cu = varlen ? cu_seqlens : nullptr;
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.hist_out = history_out;
+  a.T = (int32_t)T;
+  a.seqlen = p->seqlen;
+  a.nseq = (int32_t)nseq;
+  a.ch = (int32_t)ch;
+  a.x_dim = p->x_dim;
+  a.bc_dim = p->bc_dim;
+  a.in_stride = p->in_stride;
+  a.groups = (int32_t)(ch / 8);
+  a.tiles = (int32_t)tiles;
+  if (ssd::launch_conv(a, p->width, p->dtype == SSD_DTYPE_BF16,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(SSD_ERR_HIP, "convolution kernel launch failed");
   return SSD_OK;
 }
 

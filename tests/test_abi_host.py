@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     text = open(os.path.join(ROOT, "include", "ssd.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -250,3 +250,70 @@ def test_scan_rejects_null_and_misaligned_pointers(lib):
         ptrs = list(good)
         ptrs[i] = vp(4096 * (i + 1) + 4)
         assert _scan_status(lib, SP(), ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+
+
+def _conv_status(lib, prob, ptrs=None):
+    """ssd_conv1d_silu's status for pointer values that are never
+    dereferenced: each case is rejected (or empty) before anything is enqueued.
+    Pointer order: xbc, weight, bias, history_in, cu_seqlens, x, B, C,
+    history_out."""
+    vp = ctypes.c_void_p
+    if ptrs is None:
+        ptrs = [vp(4096 * (i + 1)) for i in range(9)]
+    return lib.ssd_conv1d_silu(ctypes.byref(prob), *ptrs, vp(None))
+
+
+def CP(**kw):
+    base = dict(batch=2, seqlen=100, num_seqs=0, x_dim=64, bc_dim=16, width=4, in_stride=96,
+                dtype=ssd.SSD_DTYPE_BF16, flags=0)
+    base.update(kw)
+    return ssd.ConvProblem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"batch": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"seqlen": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"num_seqs": -1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"x_dim": -8}, ssd.SSD_ERR_INVALID_ARG),
+    ({"flags": 1}, ssd.SSD_ERR_INVALID_ARG),
+    ({"x_dim": 0, "bc_dim": 0, "in_stride": 8}, ssd.SSD_ERR_INVALID_ARG),
+    ({"in_stride": 88}, ssd.SSD_ERR_INVALID_ARG),              # narrower than the 96 channels
+    ({"in_stride": 100}, ssd.SSD_ERR_INVALID_ARG),             # 200 bytes: not 16-byte rows
+    ({"num_seqs": 3}, ssd.SSD_ERR_INVALID_ARG),                # packed needs batch 1
+    ({"dtype": 5}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"width": 1}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"width": 5}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"x_dim": 60, "in_stride": 96}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"bc_dim": 12, "in_stride": 96}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"seqlen": 1 << 30, "batch": 4}, ssd.SSD_ERR_UNSUPPORTED),
+])
+def test_conv_validate(lib, kw, status):
+    assert _conv_status(lib, CP(**kw)) == status
+
+
+def test_conv_packed_needs_offsets(lib):
+    vp = ctypes.c_void_p
+    ptrs = [vp(4096 * (i + 1)) for i in range(9)]
+    ptrs[4] = vp(None)
+    assert _conv_status(lib, CP(batch=1, num_seqs=3), ptrs) == ssd.SSD_ERR_INVALID_ARG
+
+
+def test_conv_nothing_to_do_is_a_no_op(lib):
+    nulls = [ctypes.c_void_p(None)] * 9
+    assert _conv_status(lib, CP(batch=0), nulls) == ssd.SSD_OK
+    # no tokens and no history to write
+    assert _conv_status(lib, CP(seqlen=0), nulls) == ssd.SSD_OK
+
+
+def test_conv_rejects_null_and_misaligned_pointers(lib):
+    vp = ctypes.c_void_p
+    good = [vp(4096 * (i + 1)) for i in range(9)]
+    for i in (0, 1, 5, 6, 7):               # xbc, weight, x, B, C are required
+        ptrs = list(good)
+        ptrs[i] = vp(None)
+        assert _conv_status(lib, CP(), ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    for i in (0, 3, 5, 6, 7, 8):            # xbc, histories, x, B, C: 16-byte aligned
+        ptrs = list(good)
+        ptrs[i] = vp(4096 * (i + 1) + 8)
+        assert _conv_status(lib, CP(), ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    assert "aligned" in lib.ssd_last_error_detail().decode()
