@@ -20,7 +20,8 @@ recurrence per sequence, the state carried by the caller), a fourth,
 :mod:`oracle.selective_scan`, the Mamba-1 selective scan (a diagonal A per
 channel) that the SSD layer is compared with, and a fifth, :mod:`oracle.conv`,
 the causal depthwise convolution and activation that produce the layer's x,
-B and C, all in numpy.
+B and C, and a sixth, :mod:`oracle.backward`, the gradients of the recurrence
+(the backward pass), all in numpy.
 
 Every function here is plain and slow on purpose.
 """

@@ -262,3 +262,20 @@ def make_conv_inputs(batch: int, seqlen: int, x_dim: int, bc_dim: int, width: in
                 cu_seqlens=cu, num_seqs=0 if seq_lens is None else nseq, T=T,
                 batch=batch if seq_lens is None else 1,
                 seqlen=seqlen if seq_lens is None else T)
+
+
+def make_grad_inputs(w: Workload, inp: dict, dhT_std: float = 0.1) -> dict:
+    """Upstream gradients for the backward pass of workload ``w``: dy ~ N(0, 1)
+    in the config dtype, shaped like x, and an fp32 dL/d(final state) ~
+    N(0, dhT_std^2) shaped like the final state (None when dhT_std is 0).
+    Drawn from their own stream (seed + 500) so the forward inputs of
+    ``make_inputs(w)`` are unchanged. Draw order: dy, dhT."""
+    rng = np.random.default_rng(w.seed + 500)
+    x = inp["x"]
+    dy = rng.standard_normal(tuple(x.shape), dtype=np.float32)
+    nstate = len(inp["seq_lens"]) if inp["seq_lens"] is not None else x.shape[0]
+    dhT = None
+    if dhT_std > 0:
+        dhT = torch.from_numpy(rng.standard_normal((nstate, w.nheads, w.headdim, w.dstate),
+                                                   dtype=np.float32) * np.float32(dhT_std))
+    return dict(dy=_cast(dy, w.dtype), dhT=dhT)
