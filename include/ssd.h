@@ -176,7 +176,7 @@ ssd_status ssd_forward_dt_softplus(const ssd_problem *prob, const void *x, const
  * summed event-to-event time (kernel duration plus launch gap) in `ms`, and
  * the first-to-last event time in `total_ms`. Same arguments, outputs and
  * errors as ssd_forward; creates and destroys its own events. */
-#define SSD_MAX_STAGES 8
+#define SSD_MAX_STAGES 12
 typedef struct ssd_stage_times {
   int32_t num_stages;
   int32_t iterations;
@@ -299,6 +299,60 @@ ssd_status ssd_selective_scan(const ssd_scan_problem *prob, const void *x, const
                               const float *A, const void *B, const void *C, const float *D,
                               const float *initial_state, void *y, float *final_state,
                               void *stream);
+
+/* The backward pass: gradients of a loss L with respect to every input of
+ * ssd_forward, given dL/dy and dL/d(final state). Training recomputes the
+ * states instead of storing them (tj-hxxt.cn long read of the Mamba-1 paper,
+ * part III (3), the efficient implementation); the gradients are those of the
+ * recurrence above, through the same chunked decomposition ([QbitAI "Mamba-2"
+ * article, srwj168 repost], "Mamba-2: stronger learning, faster training and
+ * inference"). Per sequence and head, with G_t = dL/dh_t walked backwards from
+ * dL/d(final state):
+ *   G_t  += dy_t C_t^T;  dx_t = D dy_t + dt_t G_t B_t;  dB_t += dt_t G_t^T x_t
+ *   dC_t += h_t^T dy_t;  ddt_t = <G_t, x_t B_t^T> + A exp(dt_t A) <G_t, h_{t-1}>
+ *   dA   += dt_t exp(dt_t A) <G_t, h_{t-1}>;  dD += <dy_t, x_t>;  G_{t-1} = exp(dt_t A) G_t
+ * and dL/d(initial state) = G before the first token (dB, dC summed over the
+ * heads of a group). The states are recomputed from the forward inputs; the
+ * forward output is not needed.
+ *
+ * Problem: as for ssd_forward, with flags 0, dtype BF16, headdim 64, dstate
+ * 64 or 128 and chunk_size 128 or 256 (SSD_ERR_UNSUPPORTED otherwise).
+ * Arguments (device pointers owned by the caller, 16-byte aligned unless
+ * noted; shapes as in ssd_forward):
+ *   x, dt, A, B, C, D, initial_state, cu_seqlens   the forward inputs
+ *   dy             (tokens, H, P) bf16: dL/dy
+ *   dfinal_state   (batch | num_seqs, H, P, N) fp32, NULL = zero
+ *   dx             (tokens, H, P) bf16 (out)
+ *   ddt            (tokens, H) bf16 (out, any alignment), NULL = not written
+ *   dA             (H) fp32 (out, any alignment)
+ *   dB, dC         (tokens, G, N) bf16 (out)
+ *   dD             (H) fp32 (out, any alignment), NULL = not written; without D
+ *                  it is the gradient at D = 0
+ *   dinitial_state (batch | num_seqs, H, P, N) fp32 (out), NULL = not written;
+ *                  without an initial state it is the gradient at zero
+ *   workspace      at least ssd_backward_workspace_size() bytes, 256-byte
+ *                  aligned; contents on entry do not matter
+ *   stream         a hipStream_t (NULL = the default stream)
+ * Outputs must not overlap inputs or each other. Enqueues the kernels and
+ * returns; no allocation, no synchronisation. Errors as for ssd_forward. */
+ssd_status ssd_backward_workspace_size(const ssd_problem *prob, size_t *bytes);
+ssd_status ssd_backward(const ssd_problem *prob, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D,
+                        const float *initial_state, const int32_t *cu_seqlens,
+                        const void *dy, const float *dfinal_state, void *dx, void *ddt,
+                        float *dA, void *dB, void *dC, float *dD, float *dinitial_state,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ssd_backward `iterations` times back to back with a HIP event after every
+ * kernel; synchronises the stream and returns per-kernel times (ms summed
+ * over the iterations) in `times`. For measurement. */
+ssd_status ssd_backward_timed(const ssd_problem *prob, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const float *initial_state, const int32_t *cu_seqlens,
+                              const void *dy, const float *dfinal_state, void *dx, void *ddt,
+                              float *dA, void *dB, void *dC, float *dD, float *dinitial_state,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              int32_t iterations, ssd_stage_times *times);
 
 /* The convolution front that produces the SSD layer's x, B and C: a causal
  * depthwise 1-D convolution over the packed channels [x | B | C] of each

@@ -61,7 +61,7 @@ class ConvProblem(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 
-MAX_STAGES = 8
+MAX_STAGES = 12
 
 
 class StageTimes(ctypes.Structure):
@@ -80,6 +80,7 @@ class StageTimes(ctypes.Structure):
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
             "ssd_forward", "ssd_forward_dt_softplus", "ssd_forward_timed", "ssd_step",
             "ssd_selective_scan", "ssd_conv1d_silu",
+            "ssd_backward_workspace_size", "ssd_backward", "ssd_backward_timed",
             "ssd_get_workspace_layout",
             "ssd_status_string", "ssd_last_error_detail")
 
@@ -111,6 +112,10 @@ def load(path: str = LIB_PATH):
         lib.ssd_forward_dt_softplus.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
         lib.ssd_selective_scan.argtypes = [ctypes.POINTER(ScanProblem)] + [vp] * 10
         lib.ssd_conv1d_silu.argtypes = [ctypes.POINTER(ConvProblem)] + [vp] * 10
+        lib.ssd_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        lib.ssd_backward.argtypes = [P] + [vp] * 18 + [ctypes.c_size_t, vp]
+        lib.ssd_backward_timed.argtypes = ([P] + [vp] * 18 + [ctypes.c_size_t, vp,
+                                           ctypes.c_int32, ctypes.POINTER(StageTimes)])
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
                   "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step",
                   "ssd_selective_scan", "ssd_forward_dt_softplus"):
@@ -474,3 +479,97 @@ def conv1d_silu(xbc, weight, bias, x_dim, bc_dim, history=None, cu_seqlens=None,
                                   _ptr(history_out), ctypes.c_void_p(stream.cuda_stream)),
            "ssd_conv1d_silu")
     return x, B, C, history_out
+
+
+class BackwardPlan:
+    """A prepared ssd_backward call for one forward problem: the problem is
+    validated and the gradient outputs and workspace allocated once; :meth:`run`
+    only enqueues the kernels.
+
+    Takes the forward inputs (as for :class:`Plan`; bf16) and dL/dy, and
+    optionally dL/d(final state); the states are recomputed. Returns from :meth:`run` a dict
+    with dx, ddt, dA, dB, dC, dD, dinitial_state (dD without D is the gradient
+    at D = 0; dinitial_state without an initial state the gradient at zero).
+    """
+
+    def __init__(self, x, dt, A, B, C, D, initial_state, dy, dfinal_state=None,
+                 chunk_size=256, cu_seqlens=None, *, check_cu_seqlens=True):
+        if x.dim() != 4:
+            raise ValueError("x must be (batch, seqlen, nheads, headdim)")
+        batch, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        dev = x.device
+        if dev.type != "cuda":
+            raise ValueError("tensors must be on the GPU (got %s)" % dev)
+        if x.dtype != torch.bfloat16:
+            raise ValueError("the backward pass takes bfloat16 problems")
+        for name, t, shape in (("dt", dt, (batch, L, H)), ("B", B, (batch, L, G, N)),
+                               ("C", C, (batch, L, G, N)), ("dy", dy, tuple(x.shape))):
+            if tuple(t.shape) != shape or t.dtype != x.dtype or t.device != dev:
+                raise ValueError("%s must be %s %s on %s" % (name, shape, x.dtype, dev))
+        if tuple(A.shape) != (H,) or A.dtype != torch.float32:
+            raise ValueError("A must be (H,) float32")
+        if D is not None and (tuple(D.shape) != (H,) or D.dtype != torch.float32):
+            raise ValueError("D must be (H,) float32")
+        num_seqs = 0
+        if cu_seqlens is not None:
+            if batch != 1:
+                raise ValueError("cu_seqlens needs batch == 1")
+            num_seqs = int(cu_seqlens.numel()) - 1
+        nstate = num_seqs if num_seqs else batch
+        for name, t in (("initial_state", initial_state), ("dfinal_state", dfinal_state)):
+            if t is not None and (tuple(t.shape) != (nstate, H, P, N) or t.dtype != torch.float32):
+                raise ValueError("%s must be (%d, %d, %d, %d) float32" % (name, nstate, H, P, N))
+        self.prob = make_problem(batch, L, H, P, N, G, chunk_size, num_seqs, SSD_DTYPE_BF16, 0)
+        validate(self.prob)
+        self.cu = None
+        if cu_seqlens is not None:
+            if check_cu_seqlens or cu_seqlens.device.type == "cpu":
+                validate_cu_seqlens(self.prob, cu_seqlens.detach().cpu())
+            self.cu = cu_seqlens.to(device=dev, dtype=torch.int32).contiguous()
+        n = ctypes.c_size_t(0)
+        _check(load().ssd_backward_workspace_size(ctypes.byref(self.prob), ctypes.byref(n)),
+               "ssd_backward_workspace_size")
+        self.inputs = [t.contiguous() if t is not None else None
+                       for t in (x, dt, A, B, C, D, initial_state, dy, dfinal_state)]
+        self.grads = dict(
+            dx=torch.empty_like(x), ddt=torch.empty_like(dt),
+            dA=torch.empty(H, device=dev, dtype=torch.float32),
+            dB=torch.empty_like(B), dC=torch.empty_like(C),
+            dD=torch.empty(H, device=dev, dtype=torch.float32),
+            dinitial_state=torch.empty((nstate, H, P, N), device=dev, dtype=torch.float32))
+        self.workspace = torch.empty(max(n.value, 256), device=dev, dtype=torch.uint8)
+        self.tokens = batch * L
+
+    def _args(self, stream):
+        x, dt, A, B, C, D, h0, dy, dhT = self.inputs
+        g = self.grads
+        return [ctypes.byref(self.prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                _ptr(h0), _ptr(self.cu), _ptr(dy), _ptr(dhT), _ptr(g["dx"]),
+                _ptr(g["ddt"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                _ptr(g["dinitial_state"]), _ptr(self.workspace),
+                ctypes.c_size_t(self.workspace.numel()), ctypes.c_void_p(stream.cuda_stream)]
+
+    def run(self, stream=None):
+        """Enqueue one backward pass on ``stream`` (default: torch's current)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.workspace.device)
+        _check(load().ssd_backward(*self._args(stream)), "ssd_backward")
+        return self.grads
+
+    def run_timed(self, iterations: int, stream=None) -> StageTimes:
+        """``iterations`` passes with a HIP event after every kernel; waits for
+        them and returns the per-kernel times (see ssd_backward_timed)."""
+        if stream is None:
+            stream = torch.cuda.current_stream(self.workspace.device)
+        times = StageTimes()
+        _check(load().ssd_backward_timed(*self._args(stream), int(iterations),
+                                         ctypes.byref(times)), "ssd_backward_timed")
+        return times
+
+
+def backward(x, dt, A, B, C, D, initial_state, dy, dfinal_state=None, chunk_size=256,
+             cu_seqlens=None):
+    """SSD backward pass (ssd_backward): a dict of gradients (see BackwardPlan)."""
+    return BackwardPlan(x, dt, A, B, C, D, initial_state, dy, dfinal_state, chunk_size,
+                        cu_seqlens).run()

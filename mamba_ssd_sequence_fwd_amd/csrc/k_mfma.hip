@@ -26,6 +26,7 @@
 // so that the 16 rows an MFMA operand read touches fall in distinct banks.
 #include "ssd_internal.h"
 #include "mfma_common.h"
+#include "bwd.h"
 
 namespace ssd {
 
@@ -37,7 +38,11 @@ namespace ssd {
 // Three workgroups per CU fit the LDS for N <= 128; the occupancy request keeps
 // the register allocation within that (156 VGPRs for N = 128, Q = 256, where
 // the compiler otherwise takes 176 and runs two waves per SIMD).
-template <int N, int Q>
+// kDstate: the backward pass's per-chunk dstate G_c = sum_l 2^(cs_l) dy_l C_l^T,
+// the same product with x -> dy, B -> C and token weights 2^(cs_l) (the decay
+// from the chunk's entering state to token l); the caller points a.x at dy,
+// a.B at C and a.states at the output.
+template <int N, int Q, bool kDstate = false>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(N == 256 ? 2 : 3))) void k_chunk_state_mfma(Args a) {
   constexpr int QH = Q < 128 ? Q : 128;
@@ -65,8 +70,9 @@ __attribute__((amdgpu_waves_per_eu(N == 256 ? 2 : 3))) void k_chunk_state_mfma(A
     const int l = tid + 256 * q;
     if (Q >= 256 || l < Q) {
       const int lc = min(l, k.len - 1);
-      const float w = exp2_fast(last - cs[lc]) *
-                      dt_of(a, (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h], h);
+      const float w = kDstate ? exp2_fast(cs[lc])
+                              : exp2_fast(last - cs[lc]) *
+                                    dt_of(a, (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + lc) * a.H + h], h);
       sW[l] = l < k.len ? w : 0.f;
     }
   }
@@ -411,6 +417,9 @@ template <int N, int Q>
 static hipError_t launch_nq(const Args &a, bf16 *cb, hipStream_t st, int which) {
   if (which == 0) {
     hipLaunchKernelGGL((k_chunk_state_mfma<N, Q>), dim3(a.nc_max, a.H), dim3(256), 0, st, a);
+  } else if (which == 3) {
+    hipLaunchKernelGGL((k_chunk_state_mfma<N, Q, true>), dim3(a.nc_max, a.H), dim3(256), 0, st,
+                       a);
   } else if (which == 1) {
     // Small problems: one wave per tile pair, so the grid fills the GPU.
     constexpr int T = Q / 32;
@@ -450,6 +459,9 @@ static hipError_t launch_mfma(const Args &a, void *cb, hipStream_t st, int which
 
 hipError_t launch_chunk_state_mfma(const Args &a, hipStream_t st) {
   return launch_mfma(a, nullptr, st, 0);
+}
+hipError_t launch_chunk_dstate_mfma(const Args &a, hipStream_t st) {
+  return launch_mfma(a, nullptr, st, 3);
 }
 hipError_t launch_chunk_cb(const Args &a, void *cb, hipStream_t st) {
   return launch_mfma(a, cb, st, 1);

@@ -31,6 +31,7 @@
 #include "step.h"
 #include "scan.h"
 #include "conv.h"
+#include "bwd.h"
 
 namespace {
 
@@ -280,6 +281,153 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
     }
   }
 #undef SSD_LAUNCH
+  return SSD_OK;
+}
+
+// ---- backward pass -----------------------------------------------------------
+// Workspace: the per-step forward layout (plan, cs, per-chunk states), then
+// the recomputed final states, the per-chunk gradient states and the per-chunk
+// partials of dA and dD.
+struct BwdLayout {
+  ssd_problem fp;   // the problem with the per-step flag: whose layout comes first
+  Layout F;
+  size_t final_states, gst, dA_part, dD_part, total;
+};
+
+BwdLayout make_bwd_layout(const ssd_problem &p) {
+  BwdLayout B{};
+  B.fp = p;
+  B.fp.flags = SSD_FLAG_UNFUSED;
+  B.F = make_layout(B.fp);
+  const int64_t nseq = p.num_seqs > 0 ? p.num_seqs : p.batch;
+  const size_t PN = (size_t)p.headdim * p.dstate;
+  size_t off = B.F.total;
+  B.final_states = off;
+  off = round_up(off + (size_t)nseq * p.nheads * PN * sizeof(float), kAlign);
+  B.gst = off;
+  off = round_up(off + (size_t)B.F.nc_max * p.nheads * PN * sizeof(float), kAlign);
+  B.dA_part = off;
+  off = round_up(off + (size_t)B.F.nc_max * p.nheads * sizeof(float), kAlign);
+  B.dD_part = off;
+  off = round_up(off + (size_t)B.F.nc_max * p.nheads * sizeof(float), kAlign);
+  B.total = off;
+  return B;
+}
+
+ssd_status check_bwd_problem(const ssd_problem *p) {
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  if (p->flags != 0)
+    return fail(SSD_ERR_INVALID_ARG, "the backward pass takes no flags (0x%x)", p->flags);
+  if (p->dtype != SSD_DTYPE_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "the backward pass runs bf16 problems only");
+  ssd::Args a{};
+  a.P = p->headdim;
+  a.N = p->dstate;
+  a.Q = p->chunk_size;
+  if (!ssd::bwd_supports(a))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "the backward pass needs headdim 64, dstate 64 or 128 and chunk_size 128 or "
+                "256 (got %d, %d, %d)", p->headdim, p->dstate, p->chunk_size);
+  if ((int64_t)make_bwd_layout(*p).F.nc_max * p->ngroups * (p->chunk_size / ssd::kBwdRows) >
+      INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "problem too large for one launch");
+  return SSD_OK;
+}
+
+const char *const kBwdStages[] = {"plan", "chunk_cumsum", "chunk_state", "state_passing",
+                                  "chunk_dstate", "state_passing_bwd", "bwd_dx", "bwd_dbc",
+                                  "bwd_reduce"};
+
+// Enqueue the backward pass; with `ev` non-null, record ev[0] first and one
+// event after each stage that runs (names appended to `names`).
+ssd_status enqueue_bwd(const ssd::BwdArgs &b, hipStream_t s, hipEvent_t *ev,
+                       const char **names, int *count) {
+  int k = 0, n = 0;
+  auto mark = [&](const char *name) -> bool {
+    if (names) names[n] = name;
+    ++n;
+    return ev == nullptr || hipEventRecord(ev[k++], s) == hipSuccess;
+  };
+  if (ev && hipEventRecord(ev[k++], s) != hipSuccess)
+    return fail(SSD_ERR_HIP, "hipEventRecord failed");
+#define SSD_BLAUNCH(call, name)                                                      \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(SSD_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(e_)); \
+    if (!mark(name)) return fail(SSD_ERR_HIP, "hipEventRecord failed after %s", name); \
+  } while (0)
+  const ssd::Args &a = b.f;
+  if (a.varlen) SSD_BLAUNCH(ssd::launch_plan(a, s), kBwdStages[0]);
+  if (a.nc_max > 0) {
+    SSD_BLAUNCH(ssd::launch_chunk_cumsum(a, true, s), kBwdStages[1]);
+    SSD_BLAUNCH(ssd::launch_chunk_state_mfma(a, s), kBwdStages[2]);
+  }
+  SSD_BLAUNCH(ssd::launch_state_passing(a, s), kBwdStages[3]);
+  if (a.nc_max > 0) {
+    ssd::Args d = a;  // dstate: x -> dy, B -> C, output -> gst
+    d.x = b.dy;
+    d.B = a.C;
+    d.states = b.gst;
+    SSD_BLAUNCH(ssd::launch_chunk_dstate_mfma(d, s), kBwdStages[4]);
+  }
+  SSD_BLAUNCH(ssd::launch_state_passing_bwd(b, s), kBwdStages[5]);
+  if (a.nc_max > 0) {
+    SSD_BLAUNCH(ssd::launch_bwd_dx(b, s), kBwdStages[6]);
+    SSD_BLAUNCH(ssd::launch_bwd_dbc(b, s), kBwdStages[7]);
+  }
+  SSD_BLAUNCH(ssd::launch_bwd_reduce(b, s), kBwdStages[8]);
+#undef SSD_BLAUNCH
+  if (count) *count = n;
+  return SSD_OK;
+}
+
+ssd_status prepare_bwd(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D,
+                       const float *initial_state, const int32_t *cu_seqlens,
+                       const void *dy, const float *dfinal_state, void *dx, void *ddt,
+                       float *dA, void *dB, void *dC, float *dD, float *dinitial_state,
+                       void *workspace, size_t workspace_bytes, ssd::BwdArgs *out) {
+  g_detail.clear();
+  ssd_status st = check_bwd_problem(p);
+  if (st != SSD_OK) return st;
+  const bool varlen = p->num_seqs > 0;
+  const int64_t tokens = (int64_t)p->batch * p->seqlen;
+  if (!A || !dA) return fail(SSD_ERR_INVALID_ARG, "A and dA must be non-NULL");
+  if (tokens > 0 && (!x || !dt || !B || !C || !dy || !dx || !dB || !dC))
+    return fail(SSD_ERR_INVALID_ARG, "x, dt, B, C, dy, dx, dB and dC must be non-NULL");
+  if (varlen && !cu_seqlens) return fail(SSD_ERR_INVALID_ARG, "varlen needs cu_seqlens");
+  if (!varlen && cu_seqlens)
+    return fail(SSD_ERR_INVALID_ARG, "cu_seqlens given but num_seqs is 0");
+  if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) || !aligned16(dx) ||
+      !aligned16(dB) || !aligned16(dC) || !aligned16(initial_state) ||
+      !aligned16(dfinal_state) || !aligned16(dinitial_state))
+    return fail(SSD_ERR_INVALID_ARG, "x, B, C, dy, dx, dB, dC and the states must be "
+                "16-byte aligned");
+  const BwdLayout L = make_bwd_layout(*p);
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                L.total);
+  char *ws = static_cast<char *>(workspace);
+  ssd::BwdArgs b{};
+  b.f = make_args(&L.fp, L.F, x, dt, A, B, C, D, initial_state, cu_seqlens, nullptr,
+                  reinterpret_cast<float *>(ws + L.final_states), workspace);
+  b.dy = dy;
+  b.dhT = dfinal_state;
+  b.gst = reinterpret_cast<float *>(ws + L.gst);
+  b.dx = dx;
+  b.ddt = ddt;
+  b.dB = dB;
+  b.dC = dC;
+  b.dh0 = dinitial_state;
+  b.dA_part = reinterpret_cast<float *>(ws + L.dA_part);
+  b.dD_part = reinterpret_cast<float *>(ws + L.dD_part);
+  b.dA = dA;
+  b.dD = dD;
+  *out = b;
   return SSD_OK;
 }
 
@@ -559,6 +707,82 @@ ssd_status ssd_selective_scan(const ssd_scan_problem *p, const void *x, const vo
       hipSuccess)
     return fail(SSD_ERR_HIP, "selective scan kernel launch failed");
   return SSD_OK;
+}
+
+ssd_status ssd_backward_workspace_size(const ssd_problem *p, size_t *bytes) {
+  g_detail.clear();
+  ssd_status st = check_bwd_problem(p);
+  if (st != SSD_OK) return st;
+  if (!bytes) return fail(SSD_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_bwd_layout(*p).total;
+  return SSD_OK;
+}
+
+ssd_status ssd_backward(const ssd_problem *p, const void *x, const void *dt, const float *A,
+                        const void *B, const void *C, const float *D,
+                        const float *initial_state, const int32_t *cu_seqlens,
+                        const void *dy, const float *dfinal_state, void *dx, void *ddt,
+                        float *dA, void *dB, void *dC, float *dD, float *dinitial_state,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  ssd::BwdArgs b;
+  ssd_status st = prepare_bwd(p, x, dt, A, B, C, D, initial_state, cu_seqlens, dy,
+                              dfinal_state, dx, ddt, dA, dB, dC, dD, dinitial_state, workspace,
+                              workspace_bytes, &b);
+  if (st != SSD_OK) return st;
+  return enqueue_bwd(b, static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr);
+}
+
+ssd_status ssd_backward_timed(const ssd_problem *p, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              const float *initial_state, const int32_t *cu_seqlens,
+                              const void *dy, const float *dfinal_state, void *dx, void *ddt,
+                              float *dA, void *dB, void *dC, float *dD, float *dinitial_state,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              int32_t iterations, ssd_stage_times *times) {
+  if (iterations < 1 || !times)
+    return fail(SSD_ERR_INVALID_ARG, "iterations must be >= 1 and times non-NULL");
+  ssd::BwdArgs b;
+  ssd_status st = prepare_bwd(p, x, dt, A, B, C, D, initial_state, cu_seqlens, dy,
+                              dfinal_state, dx, ddt, dA, dB, dC, dD, dinitial_state, workspace,
+                              workspace_bytes, &b);
+  if (st != SSD_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  constexpr int kMax = 9;  // stages of enqueue_bwd
+  std::vector<hipEvent_t> ev((size_t)iterations * (kMax + 1), nullptr);
+  for (auto &e : ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      for (auto &f : ev) if (f) (void)hipEventDestroy(f);
+      return fail(SSD_ERR_HIP, "hipEventCreate failed");
+    }
+  const char *names[kMax] = {};
+  int ns = 0;
+  ssd_status rc = SSD_OK;
+  for (int it = 0; it < iterations && rc == SSD_OK; ++it)
+    rc = enqueue_bwd(b, s, &ev[(size_t)it * (kMax + 1)], names, &ns);
+  if (rc == SSD_OK && hipStreamSynchronize(s) != hipSuccess)
+    rc = fail(SSD_ERR_HIP, "stream synchronisation failed");
+  if (rc == SSD_OK) {
+    memset(times, 0, sizeof(*times));
+    times->num_stages = ns < SSD_MAX_STAGES ? ns : SSD_MAX_STAGES;
+    for (int k = 0; k < times->num_stages; ++k)
+      snprintf(times->names[k], sizeof(times->names[k]), "%s", names[k]);
+    float tot = 0.f;
+    for (int it = 0; it < iterations; ++it) {
+      hipEvent_t *e = &ev[(size_t)it * (kMax + 1)];
+      for (int k = 0; k < times->num_stages; ++k) {
+        float ms = 0.f;
+        (void)hipEventElapsedTime(&ms, e[k], e[k + 1]);
+        times->ms[k] += ms;
+      }
+      float t = 0.f;
+      (void)hipEventElapsedTime(&t, e[0], e[ns]);
+      tot += t;
+    }
+    times->total_ms = tot;
+    times->iterations = iterations;
+  }
+  for (auto &e : ev) (void)hipEventDestroy(e);
+  return rc;
 }
 
 ssd_status ssd_conv1d_silu(const ssd_conv_problem *p, const void *xbc, const float *weight,

@@ -317,3 +317,50 @@ def test_conv_rejects_null_and_misaligned_pointers(lib):
         ptrs[i] = vp(4096 * (i + 1) + 8)
         assert _conv_status(lib, CP(), ptrs) == ssd.SSD_ERR_INVALID_ARG, i
     assert "aligned" in lib.ssd_last_error_detail().decode()
+
+
+def _bwd_status(lib, prob, ptrs=None, ws_bytes=1 << 30):
+    """ssd_backward's status for pointer values that are never dereferenced.
+    Pointer order: x, dt, A, B, C, D, h0, cu, dy, dhT, dx, ddt, dA, dB, dC, dD,
+    dh0, workspace."""
+    vp = ctypes.c_void_p
+    if ptrs is None:
+        ptrs = [vp(4096 * (i + 1)) for i in range(18)]
+        ptrs[7] = vp(None)                        # dense: no cu_seqlens
+    return lib.ssd_backward(ctypes.byref(prob), *ptrs, ctypes.c_size_t(ws_bytes), vp(None))
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"flags": ssd.SSD_FLAG_UNFUSED}, ssd.SSD_ERR_INVALID_ARG),
+    ({"dtype": ssd.SSD_DTYPE_F32}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"headdim": 32}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"dstate": 256}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"chunk_size": 64}, ssd.SSD_ERR_UNSUPPORTED),
+    ({"nheads": 6, "ngroups": 4}, ssd.SSD_ERR_INVALID_ARG),
+])
+def test_backward_validate(lib, kw, status):
+    assert _bwd_status(lib, P(**kw)) == status
+
+
+def test_backward_workspace_size_and_checks(lib):
+    n = ctypes.c_size_t(0)
+    prob = P()
+    assert lib.ssd_backward_workspace_size(ctypes.byref(prob), ctypes.byref(n)) == ssd.SSD_OK
+    fwd = ssd.workspace_size(P(flags=ssd.SSD_FLAG_UNFUSED))
+    # the per-step forward layout plus final states, gradient states and partials
+    assert n.value >= fwd + 2 * 2 * 8 * 64 * 128 * 4
+    assert _bwd_status(lib, prob, ws_bytes=n.value - 1) == ssd.SSD_ERR_WORKSPACE
+    vp = ctypes.c_void_p
+    good = [vp(4096 * (i + 1)) for i in range(18)]
+    good[7] = vp(None)
+    for i in (0, 1, 2, 3, 4, 8, 10, 12, 13, 14):  # x dt A B C dy dx dA dB dC
+        ptrs = list(good)
+        ptrs[i] = vp(None)
+        assert _bwd_status(lib, prob, ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    for i in (0, 3, 4, 8, 9, 10, 13, 14, 16):       # 16-byte aligned tensors
+        ptrs = list(good)
+        ptrs[i] = vp(4096 * (i + 1) + 8)
+        assert _bwd_status(lib, prob, ptrs) == ssd.SSD_ERR_INVALID_ARG, i
+    ptrs = list(good)
+    ptrs[17] = vp(4096 * 18 + 128)                  # workspace not 256-byte aligned
+    assert _bwd_status(lib, prob, ptrs) == ssd.SSD_ERR_WORKSPACE
