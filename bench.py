@@ -281,6 +281,104 @@ def bench_scan(args):
     print(json.dumps(out), flush=True)
 
 
+def backward_cost(w: si.Workload, inp: dict) -> dict:
+    """Bytes and flops of each backward kernel by the method's definition
+    (unique HBM bytes; causal pairs only). The recompute stages are the
+    forward's. Per (chunk, head): dy, x, dx q*P*e; ddt q*e; fp32 states P*N*4
+    (h_in, the gradient state); per (chunk, group): B, C, dB, dC q*N*e.
+    bwd_dx does, per head, C B^T and dy x^T over the causal pairs, M^T dy, and
+    two state products (g B, h_in C); bwd_dbc does dy x^T over the causal
+    pairs and two state products per head, and Z B, Z^T C once per group."""
+    e = 2
+    lens = inp["seq_lens"] or [w.seqlen] * w.batch
+    H, P, N, G, Q = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    T = int(sum(lens))
+    chunks = [min(Q, L - c0) for L in lens for c0 in range(0, L, Q)]
+    nc, S = len(chunks), len(lens)
+    state = P * N * 4
+    causal = sum(q * (q + 1) // 2 for q in chunks)
+    f = algorithmic_cost(w, inp)
+    cost = {k: f[k] for k in ("chunk_cumsum", "chunk_state", "state_passing")}
+    cost["chunk_dstate"] = dict(bytes=T * H * P * e + T * G * N * e + T * H * 4 + nc * H * state,
+                                flops=2 * T * H * P * N)
+    cost["state_passing_bwd"] = dict(bytes=2 * nc * H * state + 2 * S * H * state,
+                                     flops=2 * nc * H * P * N)
+    cost["bwd_dx"] = dict(bytes=3 * T * H * P * e + 2 * T * H * e + 2 * T * G * N * e
+                          + 2 * nc * H * state + T * H * 4,
+                          flops=2 * causal * H * (N + 2 * P) + 4 * T * H * P * N)
+    cost["bwd_dbc"] = dict(bytes=2 * T * H * P * e + T * H * (e + 4) + 4 * T * G * N * e
+                           + 2 * nc * H * state,
+                           flops=2 * causal * H * P + 4 * T * H * P * N + 4 * causal * G * N)
+    cost["bwd_reduce"] = dict(bytes=2 * nc * H * 4 + 2 * H * 4, flops=2 * nc * H)
+    cost["plan"] = dict(bytes=0, flops=0)
+    return cost
+
+
+def bench_backward(args):
+    """Backward pass of the SSD layer on a workload config: K back-to-back
+    ssd_backward calls with a HIP event after every kernel, on the stream the
+    kernels run on. The states are recomputed inside (no forward output is
+    read)."""
+    w = si.CONFIGS[args.config]
+    inp = si.make_inputs(w)
+    gin = si.make_grad_inputs(w, inp)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev)) for k in ("x", "dt", "A", "B", "C",
+                                                                   "D", "h0")}
+    plan = ssd.BackwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                            gin["dy"].to(dev), gin["dhT"].to(dev), w.chunk, inp["cu_seqlens"])
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        plan.run(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    times = plan.run_timed(args.steps, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel_ms = times.as_dict()
+    total_ms = per_kernel_ms.pop("_total_ms")
+    ms_per_step = total_ms / args.steps
+    cost = backward_cost(w, inp)
+    kernels = {}
+    for name, ms in per_kernel_ms.items():
+        c = cost.get(name, {"bytes": 0, "flops": 0})
+        kernels[name] = {"ms": round(ms, 5), "alg_bytes": int(c["bytes"]),
+                         "alg_flops": int(c["flops"]),
+                         "GB/s": round(c["bytes"] / (ms * 1e-3) / 1e9, 1),
+                         "TFLOP/s": round(c["flops"] / (ms * 1e-3) / 1e12, 2)}
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    kd, cd = kernels[dom], cost[dom]
+    # the kernel's own roof: whichever of HBM and bf16 MFMA its algorithmic
+    # bytes and flops reach first
+    mfma_bound = cd["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) > cd["bytes"] / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": kd["TFLOP/s"],
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(kd["TFLOP/s"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(dom, "bwd-" + w.name)}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dom, "bwd-" + w.name),
+                    "mfma_frac": round(kd["TFLOP/s"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+    out = {
+        "metric": "SSD backward tokens/s (gradients of x, dt, A, B, C, D, h0; states "
+                  "recomputed)",
+        "value": round(plan.tokens / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "bwd-" + w.name, "batch": w.batch if not w.num_seqs else 1,
+                   "seq_len": plan.prob.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk,
+                   "num_seqs": w.num_seqs, "tokens_per_step": plan.tokens},
+        "roofline": roofline,
+        "kernels": kernels,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_conv(args):
     """Convolution front at the 2.7B shapes: batch 8, 2048 tokens, x 5120
     channels (80 heads x 64), B and C 128 channels each, 4 taps, bf16, with
@@ -345,6 +443,9 @@ def main():
                     help="instead of the SSD forward pass, time the Mamba-1 selective scan "
                          "(ssd_selective_scan) at the 2.7B shapes (batch 8, 2048 tokens, 5120 "
                          "channels) with state size N per channel")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward pass, time the backward pass (ssd_backward) "
+                         "on the --config workload")
     ap.add_argument("--conv", action="store_true",
                     help="instead of the SSD forward pass, time the convolution front "
                          "(ssd_conv1d_silu) at the 2.7B shapes")
@@ -384,6 +485,9 @@ def main():
         return
     if args.conv:
         bench_conv(args)
+        return
+    if args.backward:
+        bench_backward(args)
         return
 
     w = si.CONFIGS[args.config]

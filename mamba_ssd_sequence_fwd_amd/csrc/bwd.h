@@ -23,6 +23,9 @@ struct BwdArgs {
   float *dD_part;       // (chunks, H)
   float *dA;            // (H)
   float *dD;            // (H) or null
+  bf16 *hinT;           // (chunks, H, N, P): h_in as bf16, transposed (written by
+                        // the dx kernel for the dB / dC kernel)
+  bf16 *gT;             // (chunks, H, N, P): g_c likewise
 };
 
 // Row block of the dB / dC kernel (tokens per workgroup).

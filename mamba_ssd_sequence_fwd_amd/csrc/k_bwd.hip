@@ -214,6 +214,18 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
   }
   __syncthreads();
   wave0_scan<Q, false>(sCum);  // prefix sums of dt inside the chunk
+  // h_in and g_c transposed ([n][p], bf16) for the dB / dC kernel: a
+  // transposed LDS read gives each lane 8 consecutive p of one n.
+  {
+    bf16 *hT = b.hinT + ((size_t)c * a.H + h) * N * kP;
+    bf16 *gT = b.gT + ((size_t)c * a.H + h) * N * kP;
+    for (int u = wave; u < (N / 16) * (kP / 32); u += 4) {
+      const int n0 = 16 * (u % (N / 16)), p0 = 32 * (u / (N / 16));
+      const size_t off = (size_t)(n0 + lr) * kP + p0 + 8 * lg;
+      *reinterpret_cast<bf16x8 *>(hT + off) = tr_operand<N>(sHin, p0, n0);
+      *reinterpret_cast<bf16x8 *>(gT + off) = tr_operand<N>(sG, p0, n0);
+    }
+  }
 
   // dy . x per token (for dD), one token per thread.
   for (int t = tid; t < Q; t += 256) {
@@ -386,6 +398,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 //   ZC[l][s] = Z_h[l, s] for s in the block and l >= s       (feeds dB rows s)
 //   DC[n][l] += sum_p h_in[p][n] 2^(cs_l) dy[l][p]           (dC state term)
 //   DB[n][s] += sum_p g_c[p][n] dt_s 2^(cs_last - cs_s) x[s][p]  (dB state term)
+// (h_in and g_c read as the transposed bf16 copies the dx kernel wrote)
 // each Z tile computed as x . dy^T or dy . x^T over p. Z's 16 x 16 tiles are
 // taken in pairs (a 32-token K step of the final products); the 2 + 2 Q/32
 // pairs are dealt round-robin to the waves. After the last head the pairs go
@@ -394,7 +407,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 // chunk run on one XCD so the per-head operands they all read share an L2.
 // ---------------------------------------------------------------------------
 template <int N, int Q>
-__global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_dbc(BwdArgs b) {
   const Args &a = b.f;
   constexpr int R = kBwdRows;
   constexpr int NB = Q / R;
@@ -402,11 +415,14 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
   constexpr int PPW = (NPAIR + 3) / 4;
   constexpr int NTW = N / 64;          // 16-wide n tiles per wave
   constexpr int XROWS = Q + R;         // x rows [0, r0 + R) then dy rows [r0, Q)
-  __shared__ __attribute__((aligned(16))) bf16 sXD[XROWS * kP];
-  __shared__ __attribute__((aligned(16))) bf16 sHt[N * kP], sGt[N * kP];
-  __shared__ __attribute__((aligned(16))) bf16 sBC[Q * N];
-  __shared__ __attribute__((aligned(16))) bf16 sZ[NPAIR * 512];
-  __shared__ float sCs[Q], sDt[Q];
+  constexpr int BROWS = 128;           // B / C rows staged at a time in the final phase
+  // One LDS area: the per-head operands during the head loop, then the B / C
+  // rows and the Z operands (small enough for two workgroups per CU).
+  constexpr int kLoop = XROWS * kP + 2 * N * kP, kFinal = BROWS * N + NPAIR * 512;
+  __shared__ __attribute__((aligned(16))) bf16 sMem[kLoop > kFinal ? kLoop : kFinal];
+  bf16 *const sXD = sMem, *const sHt = sMem + XROWS * kP, *const sGt = sHt + N * kP;
+  bf16 *const sBC = sMem, *const sZ = sMem + BROWS * N;
+  __shared__ __attribute__((aligned(16))) float sCs[Q], sDt[Q];
 
   const int nb = gridDim.x, bid = blockIdx.x;
   const int q8 = nb >> 3, r8 = nb & 7, xcd = bid & 7;
@@ -434,8 +450,8 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
     const int h = g * a.heads_per_group + hj;
     const bf16 *xs = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
     const bf16 *dys = static_cast<const bf16 *>(b.dy) + ((size_t)k.start * a.H + h) * kP;
-    const float *hin = a.states + ((size_t)c * a.H + h) * kP * N;
-    const float *gc = b.gst + ((size_t)c * a.H + h) * kP * N;
+    const bf16 *hinT = b.hinT + ((size_t)c * a.H + h) * N * kP;
+    const bf16 *gT = b.gT + ((size_t)c * a.H + h) * N * kP;
     __syncthreads();  // the previous head's operands are consumed
     for (int it = tid; it < XROWS * (kP / 8); it += 256) {
       const int row = it / (kP / 8), col = (it % (kP / 8)) * 8;
@@ -443,18 +459,10 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
                                  : ldg8_row(dys, ldx, row - R, len, col);
       *reinterpret_cast<bf16x8 *>(sXD + rswz<kP>(row, col)) = v;
     }
-    for (int it = tid; it < kP * N / 4; it += 256) {
-      const int p = it / (N / 4), n0 = (it % (N / 4)) * 4;
-      const float4 u = *reinterpret_cast<const float4 *>(hin + (size_t)p * N + n0);
-      const float4 v = *reinterpret_cast<const float4 *>(gc + (size_t)p * N + n0);
-      sHt[rswz<kP>(n0, p)] = (bf16)u.x;
-      sHt[rswz<kP>(n0 + 1, p)] = (bf16)u.y;
-      sHt[rswz<kP>(n0 + 2, p)] = (bf16)u.z;
-      sHt[rswz<kP>(n0 + 3, p)] = (bf16)u.w;
-      sGt[rswz<kP>(n0, p)] = (bf16)v.x;
-      sGt[rswz<kP>(n0 + 1, p)] = (bf16)v.y;
-      sGt[rswz<kP>(n0 + 2, p)] = (bf16)v.z;
-      sGt[rswz<kP>(n0 + 3, p)] = (bf16)v.w;
+    for (int it = tid; it < N * (kP / 8); it += 256) {
+      const int n = it / (kP / 8), p0 = (it % (kP / 8)) * 8;
+      *reinterpret_cast<bf16x8 *>(sHt + rswz<kP>(n, p0)) = ldg8(hinT + (size_t)n * kP + p0);
+      *reinterpret_cast<bf16x8 *>(sGt + rswz<kP>(n, p0)) = ldg8(gT + (size_t)n * kP + p0);
     }
     const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
     for (int t = tid; t < Q; t += 256) {
@@ -473,6 +481,9 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
       const bool zr = q < 2 * (rb + 1);
       const int kb = zr ? q / 2 : rb + (q - 2 * (rb + 1)) / 2;
       const int half = zr ? q % 2 : (q - 2 * (rb + 1)) % 2;
+      // the column token of this pair's tiles (l for ZR, s for ZC)
+      const int coltok = r0 + 16 * half + lr;
+      const float cs_c = sCs[coltok], dt_c = sDt[coltok];
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
         const int t16 = 2 * kb + ti;   // the 16-token tile along K of the final product
@@ -487,12 +498,18 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
           const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(sXD + rswz<kP>(brow, 32 * kp + 8 * lg));
           d = mfma(av, bv, d);
         }
+        // the decay and step of this lane's four row tokens in two 16-byte reads
+        const float4 cs4 = *reinterpret_cast<const float4 *>(sCs + 16 * t16 + 4 * lg);
+        const float4 dt4 = *reinterpret_cast<const float4 *>(sDt + 16 * t16 + 4 * lg);
+        const float csr[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, dtr[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int rowtok = 16 * t16 + 4 * lg + r, coltok = r0 + 16 * half + lr;
+          const int rowtok = 16 * t16 + 4 * lg + r;
           const int s = zr ? rowtok : coltok, l = zr ? coltok : rowtok;
           const bool in = s <= l && l < len;
-          zacc[i][ti][r] += in ? d[r] * exp2_fast(sCs[min(l, len - 1)] - sCs[s]) * sDt[s] : 0.f;
+          // Z[l, s] = 2^(cs_l - cs_s) dt_s (dy_l . x_s)
+          const float f = zr ? exp2_fast(cs_c - csr[r]) * dtr[r] : exp2_fast(csr[r] - cs_c) * dt_c;
+          zacc[i][ti][r] += in ? d[r] * f : 0.f;
         }
       }
     }
@@ -524,7 +541,8 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
     }
   }
 
-  // Z pairs to LDS as column operands.
+  // Z pairs to LDS as column operands (the head loop's operands are dead).
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     const int q = wave + 4 * i;
@@ -538,21 +556,25 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
   }
   const bf16 *Bs = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
   const bf16 *Cs = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
-  // dC rows: B rows [0, r0 + R)
-  __syncthreads();
-  for (int it = tid; it < nxr * (N / 8); it += 256) {
-    const int row = it / (N / 8), col = (it % (N / 8)) * 8;
-    *reinterpret_cast<bf16x8 *>(sBC + rswz<N>(row, col)) = ldg8_row(Bs, ldb, row, len, col);
-  }
-  __syncthreads();
-  for (int kb = 0; kb <= rb; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 zv = *reinterpret_cast<const bf16x8 *>(sZ + (2 * kb + t) * 512 + lane * 8);
-#pragma unroll
-      for (int ni = 0; ni < NTW; ++ni)
-        dcacc[ni][t] = mfma(tr_operand_cb<N>(sBC, 32 * kb, 16 * (wave * NTW + ni)), zv, dcacc[ni][t]);
+  // dC rows: B rows [0, r0 + R), BROWS at a time
+  for (int b0 = 0; b0 < nxr; b0 += BROWS) {
+    __syncthreads();
+    const int nr = min(BROWS, nxr - b0);
+    for (int it = tid; it < nr * (N / 8); it += 256) {
+      const int row = it / (N / 8), col = (it % (N / 8)) * 8;
+      *reinterpret_cast<bf16x8 *>(sBC + rswz<N>(row, col)) = ldg8_row(Bs, ldb, b0 + row, len, col);
     }
+    __syncthreads();
+    for (int kb = b0 / 32; kb < (b0 + nr) / 32; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 zv = *reinterpret_cast<const bf16x8 *>(sZ + (2 * kb + t) * 512 + lane * 8);
+#pragma unroll
+        for (int ni = 0; ni < NTW; ++ni)
+          dcacc[ni][t] = mfma(tr_operand_cb<N>(sBC, 32 * kb - b0, 16 * (wave * NTW + ni)), zv,
+                              dcacc[ni][t]);
+      }
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int l = r0 + 16 * t + lr;
@@ -565,23 +587,26 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
       }
     }
   }
-  // dB rows: C rows [r0, Q) at LDS rows 0 .. Q - r0 - 1
-  __syncthreads();
-  for (int it = tid; it < (Q - r0) * (N / 8); it += 256) {
-    const int row = it / (N / 8), col = (it % (N / 8)) * 8;
-    *reinterpret_cast<bf16x8 *>(sBC + rswz<N>(row, col)) = ldg8_row(Cs, ldb, r0 + row, len, col);
-  }
-  __syncthreads();
-  for (int kb = rb; kb < NB; ++kb)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = 2 * (rb + 1) + 2 * (kb - rb) + u;
-      const bf16x8 zv = *reinterpret_cast<const bf16x8 *>(sZ + q * 512 + lane * 8);
-#pragma unroll
-      for (int ni = 0; ni < NTW; ++ni)
-        dbacc[ni][u] = mfma(tr_operand_cb<N>(sBC, 32 * (kb - rb), 16 * (wave * NTW + ni)), zv,
-                            dbacc[ni][u]);
+  // dB rows: C rows [r0, Q), BROWS at a time
+  for (int b0 = r0; b0 < Q; b0 += BROWS) {
+    __syncthreads();
+    const int nr = min(BROWS, Q - b0);
+    for (int it = tid; it < nr * (N / 8); it += 256) {
+      const int row = it / (N / 8), col = (it % (N / 8)) * 8;
+      *reinterpret_cast<bf16x8 *>(sBC + rswz<N>(row, col)) = ldg8_row(Cs, ldb, b0 + row, len, col);
     }
+    __syncthreads();
+    for (int kb = b0 / 32; kb < (b0 + nr) / 32; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = 2 * (rb + 1) + 2 * (kb - rb) + u;
+        const bf16x8 zv = *reinterpret_cast<const bf16x8 *>(sZ + q * 512 + lane * 8);
+#pragma unroll
+        for (int ni = 0; ni < NTW; ++ni)
+          dbacc[ni][u] = mfma(tr_operand_cb<N>(sBC, 32 * kb - b0, 16 * (wave * NTW + ni)), zv,
+                              dbacc[ni][u]);
+      }
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int s = r0 + 16 * u + lr;
@@ -597,26 +622,25 @@ __global__ __launch_bounds__(256) void k_bwd_dbc(BwdArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// dA and dD: sums of the per-chunk partials, one thread per head, in chunk
-// order (deterministic).
+// dA and dD: sums of the per-chunk partials, one workgroup per head, in a
+// fixed order (deterministic).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_bwd_reduce(BwdArgs b) {
+  __shared__ float red[4];
   const Args &a = b.f;
-  const int h = blockIdx.x * 256 + threadIdx.x;
-  if (h >= a.H) return;
-  int nch = 0;
-  if (a.varlen) {
-    nch = a.plan[0];
-  } else {
-    nch = a.batch * a.nc_per;
-  }
+  const int h = blockIdx.x;
+  const int nch = a.varlen ? a.plan[0] : a.batch * a.nc_per;
   float sa = 0.f, sd = 0.f;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = threadIdx.x; c < nch; c += 256) {
     sa += b.dA_part[(size_t)c * a.H + h];
     sd += b.dD_part[(size_t)c * a.H + h];
   }
-  b.dA[h] = sa;
-  if (b.dD) b.dD[h] = sd;
+  sa = block_sum(sa, red);
+  sd = block_sum(sd, red);
+  if (threadIdx.x == 0) {
+    b.dA[h] = sa;
+    if (b.dD) b.dD[h] = sd;
+  }
 }
 
 hipError_t launch_state_passing_bwd(const BwdArgs &b, hipStream_t st) {
@@ -651,7 +675,7 @@ hipError_t launch_bwd_dbc(const BwdArgs &b, hipStream_t st) {
 }
 
 hipError_t launch_bwd_reduce(const BwdArgs &b, hipStream_t st) {
-  hipLaunchKernelGGL(k_bwd_reduce, dim3((b.f.H + 255) / 256), dim3(256), 0, st, b);
+  hipLaunchKernelGGL(k_bwd_reduce, dim3(b.f.H), dim3(256), 0, st, b);
   return hipGetLastError();
 }
 

@@ -286,12 +286,13 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
 
 // ---- backward pass -----------------------------------------------------------
 // Workspace: the per-step forward layout (plan, cs, per-chunk states), then
-// the recomputed final states, the per-chunk gradient states and the per-chunk
-// partials of dA and dD.
+// the recomputed final states, the per-chunk gradient states, the per-chunk
+// partials of dA and dD, and bf16 transposed copies of the entering and
+// gradient states.
 struct BwdLayout {
   ssd_problem fp;   // the problem with the per-step flag: whose layout comes first
   Layout F;
-  size_t final_states, gst, dA_part, dD_part, total;
+  size_t final_states, gst, dA_part, dD_part, hinT, gT, total;
 };
 
 BwdLayout make_bwd_layout(const ssd_problem &p) {
@@ -310,6 +311,10 @@ BwdLayout make_bwd_layout(const ssd_problem &p) {
   off = round_up(off + (size_t)B.F.nc_max * p.nheads * sizeof(float), kAlign);
   B.dD_part = off;
   off = round_up(off + (size_t)B.F.nc_max * p.nheads * sizeof(float), kAlign);
+  B.hinT = off;
+  off = round_up(off + (size_t)B.F.nc_max * p.nheads * PN * 2, kAlign);
+  B.gT = off;
+  off = round_up(off + (size_t)B.F.nc_max * p.nheads * PN * 2, kAlign);
   B.total = off;
   return B;
 }
@@ -427,6 +432,8 @@ ssd_status prepare_bwd(const ssd_problem *p, const void *x, const void *dt, cons
   b.dD_part = reinterpret_cast<float *>(ws + L.dD_part);
   b.dA = dA;
   b.dD = dD;
+  b.hinT = reinterpret_cast<ssd::bf16 *>(ws + L.hinT);
+  b.gT = reinterpret_cast<ssd::bf16 *>(ws + L.gT);
   *out = b;
   return SSD_OK;
 }
