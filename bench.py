@@ -286,7 +286,7 @@ def backward_cost(w: si.Workload, inp: dict) -> dict:
     (unique HBM bytes; causal pairs only). The recompute stages are the
     forward's. Per (chunk, head): dy, x, dx q*P*e; ddt q*e; fp32 states P*N*4
     (h_in, the gradient state); per (chunk, group): B, C, dB, dC q*N*e.
-    bwd_dx does, per head, C B^T and dy x^T over the causal pairs, M^T dy, and
+    bwd_dx does, per head, dy x^T over the causal pairs, M^T dy, and
     two state products (g B, h_in C); bwd_dbc does dy x^T over the causal
     pairs and two state products per head, and Z B, Z^T C once per group."""
     e = 2
@@ -303,9 +303,11 @@ def backward_cost(w: si.Workload, inp: dict) -> dict:
                                 flops=2 * T * H * P * N)
     cost["state_passing_bwd"] = dict(bytes=2 * nc * H * state + 2 * S * H * state,
                                      flops=2 * nc * H * P * N)
+    cost["bwd_cbt"] = dict(bytes=2 * T * G * N * e + causal * G * 2,
+                           flops=2 * causal * G * N)
     cost["bwd_dx"] = dict(bytes=3 * T * H * P * e + 2 * T * H * e + 2 * T * G * N * e
-                          + 2 * nc * H * state + T * H * 4,
-                          flops=2 * causal * H * (N + 2 * P) + 4 * T * H * P * N)
+                          + 2 * nc * H * state + T * H * 4 + causal * G * 2,
+                          flops=4 * causal * H * P + 4 * T * H * P * N)
     cost["bwd_dbc"] = dict(bytes=2 * T * H * P * e + T * H * (e + 4) + 4 * T * G * N * e
                            + 2 * nc * H * state,
                            flops=2 * causal * H * P + 4 * T * H * P * N + 4 * causal * G * N)

@@ -34,6 +34,7 @@ constexpr int kBwdRows = 32;
 bool bwd_supports(const Args &a);
 hipError_t launch_chunk_dstate_mfma(const Args &a, hipStream_t s);
 hipError_t launch_state_passing_bwd(const BwdArgs &b, hipStream_t s);
+hipError_t launch_bwd_cbt(const BwdArgs &b, hipStream_t s);
 hipError_t launch_bwd_dx(const BwdArgs &b, hipStream_t s);
 hipError_t launch_bwd_dbc(const BwdArgs &b, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs &b, hipStream_t s);

@@ -32,6 +32,10 @@
 
 namespace ssd {
 
+// dB / dC kernel: 8 waves per workgroup (more loads in flight per CU while
+// each head's operands are staged).
+constexpr int kDbcThreads = 512;
+
 bool bwd_supports(const Args &a) {
   return a.P == kP && (a.N == 64 || a.N == 128) && (a.Q == 128 || a.Q == 256);
 }
@@ -136,11 +140,62 @@ __device__ __forceinline__ void st4(bf16 *p, const float (&v)[4]) {
 }
 
 // ---------------------------------------------------------------------------
+// C B^T of every causal 32 x 32 tile pair of a (chunk, group), once for all
+// the heads of the group, stored transposed for the dx kernel: for tile pair
+// (i, j), i >= j (l in tile i, s in tile j) and half u (s = 32 j + 16 u ..),
+// lane L holds s = 32 j + 16 u + L % 16 and eight l = 32 i + 16 (e / 4)
+// + 4 (L / 16) + (e % 4), e = 0..7: the column operand of the M^T dy product
+// in the token order of the transposed dy reads. One wave per tile pair.
+// ---------------------------------------------------------------------------
+template <int N, int Q>
+__global__ __launch_bounds__(64) void k_bwd_cbt(Args a) {
+  constexpr int KS = N / 32;
+  constexpr int T = Q / 32;
+  Chunk k;
+  const int c = blockIdx.x, g = blockIdx.y, pr = blockIdx.z;
+  if (!chunk_of(a, c, k)) return;
+  int i = 0;
+  while ((i + 1) * (i + 2) / 2 <= pr) ++i;
+  const int j = pr - i * (i + 1) / 2;
+  const int len = k.len;
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const size_t ldb = (size_t)a.G * N;
+  const bf16 *Bs = static_cast<const bf16 *>(a.B) + ((size_t)k.start * a.G + g) * N;
+  const bf16 *Cs = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
+  bf16x8 cop[2][KS], bop[2][KS];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      cop[t][ks] = ldg8_row(Cs, ldb, 32 * i + 16 * t + lr, len, 32 * ks + 8 * lg);
+      bop[t][ks] = ldg8_row(Bs, ldb, 32 * j + 16 * t + lr, len, 32 * ks + 8 * lg);
+    }
+  bf16 *dst = static_cast<bf16 *>(a.cb) +
+              ((((size_t)c * a.G + g) * (T * (T + 1) / 2) + pr) * 2) * 512;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    f32x4 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc[t] = mfma(cop[t][ks], bop[u][ks], acc[t]);
+    }
+    bf16x8 v;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * t + r] = (bf16)acc[t][r];
+    *reinterpret_cast<bf16x8 *>(dst + (size_t)u * 512 + lane * 8) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dx, ddt and the per-chunk partials of dA and dD: one workgroup (4 waves) per
 // (chunk, head). The transposed output dxd^T (p x s) is built per 16-column
-// tile of tokens s: the column operand M^T comes straight out of an MFMA
-// (C_l . B_s over n, masked and decayed in registers, in the token order of
-// the transposed dy reads), the row operand is dy^T read transposed from LDS;
+// tile of tokens s: the column operand M^T is a precomputed C B^T tile (once
+// per group, k_bwd_cbt) masked and decayed in registers, the row operand is
+// dy^T read transposed from LDS;
 // the state term adds g_c (bf16 in LDS) times B_s scaled by 2^(cs_last - cs_s).
 //
 // The decay gradient dL_t is a difference of large terms of both signs
@@ -178,6 +233,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
   const bf16 *Cs = static_cast<const bf16 *>(a.C) + ((size_t)k.start * a.G + g) * N;
   const float *gc = b.gst + ((size_t)c * a.H + h) * kP * N;
   const float *hin = a.states + ((size_t)c * a.H + h) * kP * N;
+  const bf16 *cbt = static_cast<const bf16 *>(a.cb) +
+                    ((size_t)c * a.G + g) * ((Q / 32) * (Q / 32 + 1) / 2) * 2 * 512;
   const float Dh = a.D ? a.D[h] : 0.f;
 
   // dy rows into LDS (rows past the chunk end read as zero).
@@ -188,12 +245,22 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
   }
   // g_c and h_in as bf16 [p][n]; <g_c, h_in> in fp32 on the way.
   float ghin = 0.f;
-  for (int i = tid; i < kP * N / 8; i += 256) {
+  constexpr int GI = kP * N / 8 / 256;  // 8-element pieces per thread
+  float4 gu[GI][2], hv[GI][2];
+#pragma unroll
+  for (int q = 0; q < GI; ++q) {       // every load in flight before the first use
+    const int i = tid + 256 * q;
     const int p = i / (N / 8), n0 = (i - p * (N / 8)) * 8;
-    const float4 u0 = *reinterpret_cast<const float4 *>(gc + (size_t)p * N + n0);
-    const float4 u1 = *reinterpret_cast<const float4 *>(gc + (size_t)p * N + n0 + 4);
-    const float4 v0 = *reinterpret_cast<const float4 *>(hin + (size_t)p * N + n0);
-    const float4 v1 = *reinterpret_cast<const float4 *>(hin + (size_t)p * N + n0 + 4);
+    gu[q][0] = *reinterpret_cast<const float4 *>(gc + (size_t)p * N + n0);
+    gu[q][1] = *reinterpret_cast<const float4 *>(gc + (size_t)p * N + n0 + 4);
+    hv[q][0] = *reinterpret_cast<const float4 *>(hin + (size_t)p * N + n0);
+    hv[q][1] = *reinterpret_cast<const float4 *>(hin + (size_t)p * N + n0 + 4);
+  }
+#pragma unroll
+  for (int q = 0; q < GI; ++q) {
+    const int i = tid + 256 * q;
+    const int p = i / (N / 8), n0 = (i - p * (N / 8)) * 8;
+    const float4 u0 = gu[q][0], u1 = gu[q][1], v0 = hv[q][0], v1 = hv[q][1];
     ghin += u0.x * v0.x + u0.y * v0.y + u0.z * v0.z + u0.w * v0.w + u1.x * v1.x + u1.y * v1.y +
             u1.z * v1.z + u1.w * v1.w;
     *reinterpret_cast<bf16x8 *>(sG + swz<N>(p, n0)) =
@@ -280,15 +347,21 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
     // intra-chunk terms over 32-token blocks l0 >= the block holding s0
     float colp = 0.f;
     const int nl = (len + 31) / 32;
+    // C_l . B_s for a block's 32 l (the precomputed transposed tiles), the
+    // next block's always in flight
+    auto cbt_tile = [&](int ib) {
+      return *reinterpret_cast<const bf16x8 *>(
+          cbt + ((size_t)(ib * (ib + 1) / 2 + j / 2) * 2 + (j % 2)) * 512 + lane * 8);
+    };
+    bf16x8 mdn = cbt_tile(s0 / 32);
     for (int ib = s0 / 32; ib < nl; ++ib) {
       const int l0 = 32 * ib;
-      f32x4 md[2], dyx[2];
+      const bf16x8 md = mdn;
+      if (ib + 1 < nl) mdn = cbt_tile(ib + 1);
+      f32x4 dyx[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        md[t] = dyx[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          md[t] = mfma(ldg8_row(Cs, ldb, l0 + 16 * t + lr, len, 32 * ks + 8 * lg), bB[ks], md[t]);
+        dyx[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kp = 0; kp < kP / 32; ++kp)
           dyx[t] = mfma(*reinterpret_cast<const bf16x8 *>(sDY + rswz<kP>(l0 + 16 * t + lr, 32 * kp + 8 * lg)),
@@ -302,7 +375,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
         for (int r = 0; r < 4; ++r) {
           const int l = l0 + 16 * t + 4 * lg + r;
           const bool in = sv && l >= s && l < len;
-          const float mv = in ? md[t][r] * exp2_fast(sCs[min(l, len - 1)] - cs_s) : 0.f;
+          const float mv = in ? (float)md[4 * t + r] * exp2_fast(sCs[min(l, len - 1)] - cs_s) : 0.f;
           bm[4 * t + r] = (bf16)mv;
           wv[4 * t + r] = mv * dts * dyx[t][r];
           colp += wv[4 * t + r];
@@ -310,16 +383,31 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
         acc1[pt] = mfma(tr_operand_cb<kP>(sDY, l0, 16 * pt), bm, acc1[pt]);
-      // row sums of W over this tile's 16 columns, then into sRow[l]
+      // row sums of W over this tile's 16 columns: a transposing butterfly
+      // over the 16 lanes of a row group (each step keeps half the values and
+      // adds the partner's other half), leaving lanes 2e, 2e + 1 with row e
+      {
+        float v4[4], v2[2], v1;
+        const bool b0 = lr & 1, b1 = (lr >> 1) & 1, b2 = (lr >> 2) & 1;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = wv[e];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
+        for (int m = 0; m < 4; ++m) {
+          const float keep = b0 ? wv[m + 4] : wv[m], give = b0 ? wv[m] : wv[m + 4];
+          v4[m] = keep + __shfl_xor(give, 1);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float keep = b1 ? v4[m + 2] : v4[m], give = b1 ? v4[m] : v4[m + 2];
+          v2[m] = keep + __shfl_xor(give, 2);
+        }
+        {
+          const float keep = b2 ? v2[1] : v2[0], give = b2 ? v2[0] : v2[1];
+          v1 = keep + __shfl_xor(give, 4);
+        }
+        v1 += __shfl_xor(v1, 8);
+        // lane bits (b0, b1, b2) select value index 4 b0 + 2 b1 + b2
+        const int e = 4 * b0 + 2 * b1 + b2;
         const int l = l0 + 16 * (e / 4) + 4 * lg + (e % 4);
-        if (lr == 0 && l < len) atomicAdd(&sRow[l], v);
+        if ((lr >> 3) == 0 && l < len) atomicAdd(&sRow[l], v1);
       }
     }
     colp += __shfl_xor(colp, 16);
@@ -401,21 +489,23 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 // (h_in and g_c read as the transposed bf16 copies the dx kernel wrote)
 // each Z tile computed as x . dy^T or dy . x^T over p. Z's 16 x 16 tiles are
 // taken in pairs (a 32-token K step of the final products); the 2 + 2 Q/32
-// pairs are dealt round-robin to the waves. After the last head the pairs go
+// pairs, and the (n tile, half) tiles of DC and DB, are dealt round-robin to
+// the 8 waves. After the last head the pairs go
 // to LDS as bf16 column operands in the token order of the transposed B / C
 // reads, and DC += B^T-ZR, DB += C^T-ZC finish the sums. Workgroups of one
 // chunk run on one XCD so the per-head operands they all read share an L2.
 // ---------------------------------------------------------------------------
 template <int N, int Q>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_dbc(BwdArgs b) {
+__global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
   const Args &a = b.f;
+  constexpr int NW = kDbcThreads / 64;  // waves
   constexpr int R = kBwdRows;
   constexpr int NB = Q / R;
   constexpr int NPAIR = 2 + 2 * NB;
-  constexpr int PPW = (NPAIR + 3) / 4;
-  constexpr int NTW = N / 64;          // 16-wide n tiles per wave
-  constexpr int XROWS = Q + R;         // x rows [0, r0 + R) then dy rows [r0, Q)
-  constexpr int BROWS = 128;           // B / C rows staged at a time in the final phase
+  constexpr int PPW = (NPAIR + NW - 1) / NW;
+  constexpr int UPW = (N / 16) * 2 / NW;  // (n tile, half) units of DC and DB per wave
+  constexpr int XROWS = Q + R;            // x rows [0, r0 + R) then dy rows [r0, Q)
+  constexpr int BROWS = 128;              // B / C rows staged at a time in the final phase
   // One LDS area: the per-head operands during the head loop, then the B / C
   // rows and the Z operands (small enough for two workgroups per CU).
   constexpr int kLoop = XROWS * kP + 2 * N * kP, kFinal = BROWS * N + NPAIR * 512;
@@ -438,45 +528,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N;
   const int nxr = r0 + R;              // x rows staged
 
-  f32x4 zacc[PPW][2], dcacc[NTW][2], dbacc[NTW][2];
+  f32x4 zacc[PPW][2], dcacc[UPW], dbacc[UPW];
 #pragma unroll
   for (int i = 0; i < PPW; ++i) zacc[i][0] = zacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < NTW; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) dcacc[i][t] = dbacc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < UPW; ++i) dcacc[i] = dbacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int hj = 0; hj < a.heads_per_group; ++hj) {
-    const int h = g * a.heads_per_group + hj;
+  // Per-head operands staged through registers: the next head's loads are
+  // issued before the current head's products, so their latency overlaps.
+  constexpr int XI = (XROWS * (kP / 8) + kDbcThreads - 1) / kDbcThreads;
+  constexpr int HI = (N * (kP / 8) + kDbcThreads - 1) / kDbcThreads;
+  constexpr int TI = (Q + kDbcThreads - 1) / kDbcThreads;
+  bf16x8 vx[XI], vh[HI], vg[HI];
+  float vcs[TI], vdt[TI];
+  auto fetch = [&](int h) {
     const bf16 *xs = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
     const bf16 *dys = static_cast<const bf16 *>(b.dy) + ((size_t)k.start * a.H + h) * kP;
     const bf16 *hinT = b.hinT + ((size_t)c * a.H + h) * N * kP;
     const bf16 *gT = b.gT + ((size_t)c * a.H + h) * N * kP;
-    __syncthreads();  // the previous head's operands are consumed
-    for (int it = tid; it < XROWS * (kP / 8); it += 256) {
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int it = tid + i * kDbcThreads;
       const int row = it / (kP / 8), col = (it % (kP / 8)) * 8;
-      const bf16x8 v = row < nxr ? ldg8_row(xs, ldx, row, len, col)
-                                 : ldg8_row(dys, ldx, row - R, len, col);
-      *reinterpret_cast<bf16x8 *>(sXD + rswz<kP>(row, col)) = v;
+      if (it < XROWS * (kP / 8))
+        vx[i] = row < nxr ? ldg8_row(xs, ldx, row, len, col) : ldg8_row(dys, ldx, row - R, len, col);
     }
-    for (int it = tid; it < N * (kP / 8); it += 256) {
+#pragma unroll
+    for (int i = 0; i < HI; ++i) {
+      const int it = tid + i * kDbcThreads;
       const int n = it / (kP / 8), p0 = (it % (kP / 8)) * 8;
-      *reinterpret_cast<bf16x8 *>(sHt + rswz<kP>(n, p0)) = ldg8(hinT + (size_t)n * kP + p0);
-      *reinterpret_cast<bf16x8 *>(sGt + rswz<kP>(n, p0)) = ldg8(gT + (size_t)n * kP + p0);
+      if (it < N * (kP / 8)) {
+        vh[i] = ldg8(hinT + (size_t)n * kP + p0);
+        vg[i] = ldg8(gT + (size_t)n * kP + p0);
+      }
     }
     const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
-    for (int t = tid; t < Q; t += 256) {
-      sCs[t] = cs[min(t, len - 1)];
-      sDt[t] = t < len ? (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h]
-                       : 0.f;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int t = tid + i * kDbcThreads;
+      if (t < Q) {
+        vcs[i] = cs[min(t, len - 1)];
+        vdt[i] = t < len ? (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h]
+                         : 0.f;
+      }
+    }
+  };
+  fetch(g * a.heads_per_group);
+  for (int hj = 0; hj < a.heads_per_group; ++hj) {
+    __syncthreads();  // the previous head's operands are consumed
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int it = tid + i * kDbcThreads;
+      if (it < XROWS * (kP / 8))
+        *reinterpret_cast<bf16x8 *>(sXD + rswz<kP>(it / (kP / 8), (it % (kP / 8)) * 8)) = vx[i];
+    }
+#pragma unroll
+    for (int i = 0; i < HI; ++i) {
+      const int it = tid + i * kDbcThreads;
+      if (it < N * (kP / 8)) {
+        const int n = it / (kP / 8), p0 = (it % (kP / 8)) * 8;
+        *reinterpret_cast<bf16x8 *>(sHt + rswz<kP>(n, p0)) = vh[i];
+        *reinterpret_cast<bf16x8 *>(sGt + rswz<kP>(n, p0)) = vg[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int t = tid + i * kDbcThreads;
+      if (t < Q) {
+        sCs[t] = vcs[i];
+        sDt[t] = vdt[i];
+      }
     }
     __syncthreads();
+    if (hj + 1 < a.heads_per_group) fetch(g * a.heads_per_group + hj + 1);
     const float cs_last = sCs[len - 1];
 
     // Z pairs of this wave
 #pragma unroll
     for (int i = 0; i < PPW; ++i) {
-      const int q = wave + 4 * i;
+      const int q = wave + NW * i;
       if (q >= NPAIR) break;
       const bool zr = q < 2 * (rb + 1);
       const int kb = zr ? q / 2 : rb + (q - 2 * (rb + 1)) / 2;
@@ -513,12 +643,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
       }
     }
-    // state terms: DC[n][l] (l = r0 + 16 t + lr) and DB[n][s] (s = r0 + 16 u + lr)
+    // state terms of this wave's units (n tile, half): DC[n][l], l = r0 + 16 half + lr,
+    // and DB[n][s], s = r0 + 16 half + lr
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int tok = r0 + 16 * t + lr;
+    for (int ui = 0; ui < UPW; ++ui) {
+      const int u = wave + NW * ui, nt = u >> 1, half = u & 1;
+      const int tok = r0 + 16 * half + lr;
       const float el = tok < len ? exp2_fast(sCs[tok]) : 0.f;
       const float es = tok < len ? sDt[tok] * exp2_fast(cs_last - sCs[tok]) : 0.f;
+      const int n = 16 * nt + lr;
 #pragma unroll
       for (int kp = 0; kp < kP / 32; ++kp) {
         const bf16x8 dyv = *reinterpret_cast<const bf16x8 *>(sXD + rswz<kP>(R + tok, 32 * kp + 8 * lg));
@@ -529,14 +662,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
           dyb[e] = (bf16)((float)dyv[e] * el);
           xb[e] = (bf16)((float)xv[e] * es);
         }
-#pragma unroll
-        for (int ni = 0; ni < NTW; ++ni) {
-          const int n = 16 * (wave * NTW + ni) + lr;
-          dcacc[ni][t] = mfma(*reinterpret_cast<const bf16x8 *>(sHt + rswz<kP>(n, 32 * kp + 8 * lg)),
-                              dyb, dcacc[ni][t]);
-          dbacc[ni][t] = mfma(*reinterpret_cast<const bf16x8 *>(sGt + rswz<kP>(n, 32 * kp + 8 * lg)),
-                              xb, dbacc[ni][t]);
-        }
+        dcacc[ui] = mfma(*reinterpret_cast<const bf16x8 *>(sHt + rswz<kP>(n, 32 * kp + 8 * lg)),
+                         dyb, dcacc[ui]);
+        dbacc[ui] = mfma(*reinterpret_cast<const bf16x8 *>(sGt + rswz<kP>(n, 32 * kp + 8 * lg)),
+                         xb, dbacc[ui]);
       }
     }
   }
@@ -545,7 +674,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
-    const int q = wave + 4 * i;
+    const int q = wave + NW * i;
     if (q >= NPAIR) break;
     bf16x8 v;
 #pragma unroll
@@ -560,63 +689,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int b0 = 0; b0 < nxr; b0 += BROWS) {
     __syncthreads();
     const int nr = min(BROWS, nxr - b0);
-    for (int it = tid; it < nr * (N / 8); it += 256) {
+    for (int it = tid; it < nr * (N / 8); it += kDbcThreads) {
       const int row = it / (N / 8), col = (it % (N / 8)) * 8;
       *reinterpret_cast<bf16x8 *>(sBC + rswz<N>(row, col)) = ldg8_row(Bs, ldb, b0 + row, len, col);
     }
     __syncthreads();
     for (int kb = b0 / 32; kb < (b0 + nr) / 32; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int ui = 0; ui < UPW; ++ui) {
+        const int u = wave + NW * ui, nt = u >> 1, t = u & 1;
         const bf16x8 zv = *reinterpret_cast<const bf16x8 *>(sZ + (2 * kb + t) * 512 + lane * 8);
-#pragma unroll
-        for (int ni = 0; ni < NTW; ++ni)
-          dcacc[ni][t] = mfma(tr_operand_cb<N>(sBC, 32 * kb - b0, 16 * (wave * NTW + ni)), zv,
-                              dcacc[ni][t]);
+        dcacc[ui] = mfma(tr_operand_cb<N>(sBC, 32 * kb - b0, 16 * nt), zv, dcacc[ui]);
       }
   }
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int ui = 0; ui < UPW; ++ui) {
+    const int u = wave + NW * ui, nt = u >> 1, t = u & 1;
     const int l = r0 + 16 * t + lr;
     if (l < len) {
       bf16 *dst = static_cast<bf16 *>(b.dC) + ((size_t)(k.start + l) * a.G + g) * N;
-#pragma unroll
-      for (int ni = 0; ni < NTW; ++ni) {
-        float o[4] = {dcacc[ni][t][0], dcacc[ni][t][1], dcacc[ni][t][2], dcacc[ni][t][3]};
-        st4(dst + 16 * (wave * NTW + ni) + 4 * lg, o);
-      }
+      float o[4] = {dcacc[ui][0], dcacc[ui][1], dcacc[ui][2], dcacc[ui][3]};
+      st4(dst + 16 * nt + 4 * lg, o);
     }
   }
   // dB rows: C rows [r0, Q), BROWS at a time
   for (int b0 = r0; b0 < Q; b0 += BROWS) {
     __syncthreads();
     const int nr = min(BROWS, Q - b0);
-    for (int it = tid; it < nr * (N / 8); it += 256) {
+    for (int it = tid; it < nr * (N / 8); it += kDbcThreads) {
       const int row = it / (N / 8), col = (it % (N / 8)) * 8;
       *reinterpret_cast<bf16x8 *>(sBC + rswz<N>(row, col)) = ldg8_row(Cs, ldb, b0 + row, len, col);
     }
     __syncthreads();
     for (int kb = b0 / 32; kb < (b0 + nr) / 32; ++kb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int q = 2 * (rb + 1) + 2 * (kb - rb) + u;
+      for (int ui = 0; ui < UPW; ++ui) {
+        const int u = wave + NW * ui, nt = u >> 1, half = u & 1;
+        const int q = 2 * (rb + 1) + 2 * (kb - rb) + half;
         const bf16x8 zv = *reinterpret_cast<const bf16x8 *>(sZ + q * 512 + lane * 8);
-#pragma unroll
-        for (int ni = 0; ni < NTW; ++ni)
-          dbacc[ni][u] = mfma(tr_operand_cb<N>(sBC, 32 * kb - b0, 16 * (wave * NTW + ni)), zv,
-                              dbacc[ni][u]);
+        dbacc[ui] = mfma(tr_operand_cb<N>(sBC, 32 * kb - b0, 16 * nt), zv, dbacc[ui]);
       }
   }
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int s = r0 + 16 * u + lr;
+  for (int ui = 0; ui < UPW; ++ui) {
+    const int u = wave + NW * ui, nt = u >> 1, half = u & 1;
+    const int s = r0 + 16 * half + lr;
     if (s < len) {
       bf16 *dst = static_cast<bf16 *>(b.dB) + ((size_t)(k.start + s) * a.G + g) * N;
-#pragma unroll
-      for (int ni = 0; ni < NTW; ++ni) {
-        float o[4] = {dbacc[ni][u][0], dbacc[ni][u][1], dbacc[ni][u][2], dbacc[ni][u][3]};
-        st4(dst + 16 * (wave * NTW + ni) + 4 * lg, o);
-      }
+      float o[4] = {dbacc[ui][0], dbacc[ui][1], dbacc[ui][2], dbacc[ui][3]};
+      st4(dst + 16 * nt + 4 * lg, o);
     }
   }
 }
@@ -652,6 +773,19 @@ hipError_t launch_state_passing_bwd(const BwdArgs &b, hipStream_t st) {
 }
 
 template <int N, int Q>
+static hipError_t launch_cbt_nq(const BwdArgs &b, hipStream_t st) {
+  constexpr int T = Q / 32;
+  hipLaunchKernelGGL((k_bwd_cbt<N, Q>), dim3(b.f.nc_max, b.f.G, T * (T + 1) / 2), dim3(64), 0,
+                     st, b.f);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_cbt(const BwdArgs &b, hipStream_t st) {
+  if (b.f.N == 64) return b.f.Q == 128 ? launch_cbt_nq<64, 128>(b, st) : launch_cbt_nq<64, 256>(b, st);
+  return b.f.Q == 128 ? launch_cbt_nq<128, 128>(b, st) : launch_cbt_nq<128, 256>(b, st);
+}
+
+template <int N, int Q>
 static hipError_t launch_dx_nq(const BwdArgs &b, hipStream_t st) {
   hipLaunchKernelGGL((k_bwd_dx<N, Q>), dim3(b.f.nc_max, b.f.H), dim3(256), 0, st, b);
   return hipGetLastError();
@@ -665,7 +799,7 @@ hipError_t launch_bwd_dx(const BwdArgs &b, hipStream_t st) {
 template <int N, int Q>
 static hipError_t launch_dbc_nq(const BwdArgs &b, hipStream_t st) {
   const int64_t blocks = (int64_t)b.f.nc_max * b.f.G * (Q / kBwdRows);
-  hipLaunchKernelGGL((k_bwd_dbc<N, Q>), dim3((unsigned)blocks), dim3(256), 0, st, b);
+  hipLaunchKernelGGL((k_bwd_dbc<N, Q>), dim3((unsigned)blocks), dim3(kDbcThreads), 0, st, b);
   return hipGetLastError();
 }
 

@@ -341,8 +341,8 @@ ssd_status check_bwd_problem(const ssd_problem *p) {
 }
 
 const char *const kBwdStages[] = {"plan", "chunk_cumsum", "chunk_state", "state_passing",
-                                  "chunk_dstate", "state_passing_bwd", "bwd_dx", "bwd_dbc",
-                                  "bwd_reduce"};
+                                  "chunk_dstate", "state_passing_bwd", "bwd_cbt", "bwd_dx",
+                                  "bwd_dbc", "bwd_reduce"};
 
 // Enqueue the backward pass; with `ev` non-null, record ev[0] first and one
 // event after each stage that runs (names appended to `names`).
@@ -379,10 +379,11 @@ ssd_status enqueue_bwd(const ssd::BwdArgs &b, hipStream_t s, hipEvent_t *ev,
   }
   SSD_BLAUNCH(ssd::launch_state_passing_bwd(b, s), kBwdStages[5]);
   if (a.nc_max > 0) {
-    SSD_BLAUNCH(ssd::launch_bwd_dx(b, s), kBwdStages[6]);
-    SSD_BLAUNCH(ssd::launch_bwd_dbc(b, s), kBwdStages[7]);
+    SSD_BLAUNCH(ssd::launch_bwd_cbt(b, s), kBwdStages[6]);
+    SSD_BLAUNCH(ssd::launch_bwd_dx(b, s), kBwdStages[7]);
+    SSD_BLAUNCH(ssd::launch_bwd_dbc(b, s), kBwdStages[8]);
   }
-  SSD_BLAUNCH(ssd::launch_bwd_reduce(b, s), kBwdStages[8]);
+  SSD_BLAUNCH(ssd::launch_bwd_reduce(b, s), kBwdStages[9]);
 #undef SSD_BLAUNCH
   if (count) *count = n;
   return SSD_OK;
@@ -754,7 +755,7 @@ ssd_status ssd_backward_timed(const ssd_problem *p, const void *x, const void *d
                               workspace_bytes, &b);
   if (st != SSD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int kMax = 9;  // stages of enqueue_bwd
+  constexpr int kMax = 10;  // stages of enqueue_bwd
   std::vector<hipEvent_t> ev((size_t)iterations * (kMax + 1), nullptr);
   for (auto &e : ev)
     if (hipEventCreate(&e) != hipSuccess) {
