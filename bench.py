@@ -90,6 +90,8 @@ TRAFFIC_PROFILES = {
                                        ("k_step.hip", "step.h", "ssd_internal.h")),
     ("ssd_conv", "conv-front-2.7b"): ("ssd_conv_front-2.7b.md",
                                       ("k_conv.hip", "conv.h", "ssd_internal.h")),
+    ("bwd_dbc", "bwd-2.7b-bf16"): ("ssd_backward_2.7b-bf16.md",
+                                   ("k_bwd.hip", "bwd.h", "mfma_common.h", "ssd_internal.h")),
 }
 
 
@@ -305,11 +307,14 @@ def backward_cost(w: si.Workload, inp: dict) -> dict:
                                      flops=2 * nc * H * P * N)
     cost["bwd_cbt"] = dict(bytes=2 * T * G * N * e + causal * G * 2,
                            flops=2 * causal * G * N)
+    # bwd_dx also writes bf16 transposed copies of h_in and g (P*N*2 each per
+    # (chunk, head)), which bwd_dbc reads in place of the fp32 states
     cost["bwd_dx"] = dict(bytes=3 * T * H * P * e + 2 * T * H * e + 2 * T * G * N * e
-                          + 2 * nc * H * state + T * H * 4 + causal * G * 2,
+                          + 2 * nc * H * state + T * H * 4 + causal * G * 2
+                          + 2 * nc * H * P * N * 2,
                           flops=4 * causal * H * P + 4 * T * H * P * N)
     cost["bwd_dbc"] = dict(bytes=2 * T * H * P * e + T * H * (e + 4) + 4 * T * G * N * e
-                           + 2 * nc * H * state,
+                           + 2 * nc * H * P * N * 2,
                            flops=2 * causal * H * P + 4 * T * H * P * N + 4 * causal * G * N)
     cost["bwd_reduce"] = dict(bytes=2 * nc * H * 4 + 2 * H * 4, flops=2 * nc * H)
     cost["plan"] = dict(bytes=0, flops=0)
