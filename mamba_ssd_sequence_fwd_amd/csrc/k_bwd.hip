@@ -536,11 +536,17 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
 
   // Per-head operands staged through registers: the next head's loads are
   // issued before the current head's products, so their latency overlaps.
+  // Every load is unconditional (indices clamped; only the LDS stores are
+  // guarded), and nothing converts or selects a loaded value before the
+  // store, so the compiler has no reason to wait for them early. Rows past
+  // the chunk end hold copies of its last row: every product that reads
+  // them is masked (l < len) or scaled by zero.
   constexpr int XI = (XROWS * (kP / 8) + kDbcThreads - 1) / kDbcThreads;
   constexpr int HI = (N * (kP / 8) + kDbcThreads - 1) / kDbcThreads;
   constexpr int TI = (Q + kDbcThreads - 1) / kDbcThreads;
   bf16x8 vx[XI], vh[HI], vg[HI];
-  float vcs[TI], vdt[TI];
+  float vcs[TI];
+  bf16 vdt[TI];
   auto fetch = [&](int h) {
     const bf16 *xs = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
     const bf16 *dys = static_cast<const bf16 *>(b.dy) + ((size_t)k.start * a.H + h) * kP;
@@ -548,29 +554,25 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
     const bf16 *gT = b.gT + ((size_t)c * a.H + h) * N * kP;
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-      const int it = tid + i * kDbcThreads;
+      const int it = min(tid + i * kDbcThreads, XROWS * (kP / 8) - 1);
       const int row = it / (kP / 8), col = (it % (kP / 8)) * 8;
-      if (it < XROWS * (kP / 8))
-        vx[i] = row < nxr ? ldg8_row(xs, ldx, row, len, col) : ldg8_row(dys, ldx, row - R, len, col);
+      const bf16 *src = row < nxr ? xs + (size_t)min(row, len - 1) * ldx
+                                  : dys + (size_t)min(row - R, len - 1) * ldx;
+      vx[i] = ldg8(src + col);
     }
 #pragma unroll
     for (int i = 0; i < HI; ++i) {
-      const int it = tid + i * kDbcThreads;
+      const int it = min(tid + i * kDbcThreads, N * (kP / 8) - 1);
       const int n = it / (kP / 8), p0 = (it % (kP / 8)) * 8;
-      if (it < N * (kP / 8)) {
-        vh[i] = ldg8(hinT + (size_t)n * kP + p0);
-        vg[i] = ldg8(gT + (size_t)n * kP + p0);
-      }
+      vh[i] = ldg8(hinT + (size_t)n * kP + p0);
+      vg[i] = ldg8(gT + (size_t)n * kP + p0);
     }
     const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const int t = tid + i * kDbcThreads;
-      if (t < Q) {
-        vcs[i] = cs[min(t, len - 1)];
-        vdt[i] = t < len ? (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h]
-                         : 0.f;
-      }
+      const int t = min(min(tid + i * kDbcThreads, Q - 1), len - 1);
+      vcs[i] = cs[t];
+      vdt[i] = static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
     }
   };
   fetch(g * a.heads_per_group);
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
       const int t = tid + i * kDbcThreads;
       if (t < Q) {
         sCs[t] = vcs[i];
-        sDt[t] = vdt[i];
+        sDt[t] = t < len ? (float)vdt[i] : 0.f;
       }
     }
     __syncthreads();
