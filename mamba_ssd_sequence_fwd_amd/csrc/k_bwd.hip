@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
   const int c = blockIdx.x;
   if (!chunk_of(a, c, k)) return;
   const int h = blockIdx.y, g = h / a.heads_per_group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lr = lane & 15, lg = lane >> 4;
   const int len = k.len;
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N;
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
     for (int ib = s0 / 32; ib < nl; ++ib) {
       const int l0 = 32 * ib;
       const bf16x8 md = mdn;
-      if (ib + 1 < nl) mdn = cbt_tile(ib + 1);
+      mdn = cbt_tile(min(ib + 1, nl - 1));  // unconditional, so it stays in flight
       f32x4 dyx[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -367,18 +368,24 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
           dyx[t] = mfma(*reinterpret_cast<const bf16x8 *>(sDY + rswz<kP>(l0 + 16 * t + lr, 32 * kp + 8 * lg)),
                         bX[kp], dyx[t]);
       }
+      // the decay prefix of this lane's 8 row tokens: two 16-byte LDS reads,
+      // no per-element branch (sCs past the chunk end repeats its last value;
+      // masked entries are dropped by a select, never multiplied)
+      const float4 c0 = *reinterpret_cast<const float4 *>(sCs + l0 + 4 * lg);
+      const float4 c1 = *reinterpret_cast<const float4 *>(sCs + l0 + 16 + 4 * lg);
+      const float csl[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
       bf16x8 bm;
       float wv[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int l = l0 + 16 * t + 4 * lg + r;
+          const int e = 4 * t + r, l = l0 + 16 * t + 4 * lg + r;
           const bool in = sv && l >= s && l < len;
-          const float mv = in ? (float)md[4 * t + r] * exp2_fast(sCs[min(l, len - 1)] - cs_s) : 0.f;
-          bm[4 * t + r] = (bf16)mv;
-          wv[4 * t + r] = mv * dts * dyx[t][r];
-          colp += wv[4 * t + r];
+          const float mv = (float)md[e] * exp2_fast(csl[e] - cs_s);
+          bm[e] = (bf16)(in ? mv : 0.f);
+          wv[e] = in ? mv * dts * dyx[t][r] : 0.f;
+          colp += wv[e];
         }
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
@@ -523,7 +530,8 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
   if (c >= a.nc_max || !chunk_of(a, c, k)) return;
   const int len = k.len, r0 = R * rb;
   if (r0 >= len) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lr = lane & 15, lg = lane >> 4;
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N;
   const int nxr = r0 + R;              // x rows staged
