@@ -303,9 +303,16 @@ __device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, c
   }
 }
 
-template <int N, int Q>
+// kDeep: every B^T tile of step 2 is loaded up front instead of four steps
+// ahead, at two workgroups per CU instead of three (more registers). When a
+// problem has no more work units than the chip holds at once, each
+// workgroup's own latency is the whole time and this wins (config-1 shapes:
+// 66 -> 56 us); with many units per slot the third workgroup per CU hides
+// that latency better (the 2.7B shapes: equal; long packed input: 13%
+// slower), so the launcher picks it by grid size.
+template <int N, int Q, bool kDeep>
 __global__ __launch_bounds__(64 * kChainWaves)
-__attribute__((amdgpu_waves_per_eu(N == 256 ? 2 : 3, N == 256 ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(N == 256 || kDeep ? 2 : 3, N == 256 || kDeep ? 2 : 3)))
 void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   constexpr int T = Q / 32, PAIRS = T * (T + 1) / 2, NKS = Q / 32;
   constexpr int NTW = N / 64;                 // 16-row n tiles of the state per wave
@@ -369,7 +376,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   const int nt0 = wave * NTW;
   // This wave's B^T operand tiles (n tiles nt0..), streamed KPF 32-token
   // steps ahead of their use; the first KPF steps now.
-  constexpr int KPF = NKS < 4 ? NKS : 4;
+  constexpr int KPF = kDeep ? NKS : (NKS < 4 ? NKS : 4);
   const bf16 *btc = bt + (((size_t)c * a.G + g) * (N / 16) + nt0) * NKS * 512 + lane * 8;
   bf16x8 bts[NTW][KPF];
 #pragma unroll
@@ -548,13 +555,25 @@ bool chain_path_supports(const Args &a) {
          (a.N == 64 || a.N == 128 || a.N == 256);
 }
 
+// Work units up to which the deep-prefetch kernel is used: what 256 CUs hold
+// at three workgroups each.
+constexpr int64_t kDeepMaxUnits = 3 * 256;
+
 template <int N, int Q>
 static hipError_t launch_chain_nq(const Args &a, const void *cb, const void *bt,
                                   hipStream_t st) {
   const int64_t blocks = (int64_t)a.nc_max * a.H;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_ssd_chain<N, Q>), dim3((unsigned)blocks), dim3(64 * kChainWaves), 0, st,
-                     a, static_cast<const bf16 *>(cb), static_cast<const bf16 *>(bt));
+  const bf16 *cbp = static_cast<const bf16 *>(cb), *btp = static_cast<const bf16 *>(bt);
+  if constexpr (N != 256) {  // at N = 256 the deep variant does not fit the registers
+    if (blocks <= kDeepMaxUnits) {
+      hipLaunchKernelGGL((k_ssd_chain<N, Q, true>), dim3((unsigned)blocks),
+                         dim3(64 * kChainWaves), 0, st, a, cbp, btp);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_ssd_chain<N, Q, false>), dim3((unsigned)blocks), dim3(64 * kChainWaves),
+                     0, st, a, cbp, btp);
   return hipGetLastError();
 }
 

@@ -39,6 +39,10 @@ SMALL = {
     # kernel stages each chunk's B in LDS
     "staged-cb-G4-N64": si.scaled(C[3], batch=1, seqlen=16500, nheads=8, ngroups=4,
                                   dstate=64, seed=2025),
+    # more work units (chunks x heads) than the chip holds at once: the chained
+    # kernel's three-per-CU variant (smaller grids take the deep-prefetch one)
+    "many-units-N128": si.scaled(C[2], batch=2, seqlen=1800, nheads=52, seed=2026),
+    "many-units-N64-h0": si.scaled(C[2], batch=4, seqlen=1000, nheads=64, dstate=64, seed=2027),
     "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
                               chunk=128, seed=2021),
     "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
