@@ -32,6 +32,11 @@ CASES = {
                                 log_neg_a=(-7.0, -5.0), seed=5004),
     "no-D-no-h0": si.scaled(BASE, batch=2, seqlen=256, nheads=2, h0_std=0.0, seed=5005),
     "single-chunk-Q256": si.scaled(BASE, batch=3, seqlen=100, nheads=2, seed=5006),
+    # the dB / dC kernel walks a group's heads in pairs: an odd count and a
+    # single head take its tail path
+    "odd-heads-per-group": si.scaled(BASE, batch=1, seqlen=400, nheads=3, seed=5007),
+    "one-head-N64-Q128": si.scaled(BASE, batch=2, seqlen=200, nheads=1, dstate=64, chunk=128,
+                                   seed=5008),
 }
 
 
