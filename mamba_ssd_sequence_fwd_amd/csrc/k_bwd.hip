@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// dB and dC: one workgroup (4 waves) per (chunk, group, block of kBwdRows
+// dB and dC: one workgroup (8 waves) per (chunk, group, block of kBwdRows
 // tokens r0 .. r0 + 31), summing over the heads of the group. Per head it
 // adds, into fp32 accumulators:
 //   ZR[s][l] = Z_h[l, s] for l in the block and s <= l       (feeds dC rows l)
