@@ -480,8 +480,19 @@ def main():
         for _ in range(max(args.steps, 1)):
             dst.copy_(src)
         torch.cuda.synchronize()
+        # the same copy timed (events on torch's stream, which runs it): the
+        # HBM rate a plain streaming read + write reaches on this GPU
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / max(args.steps, 1)
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
-                          "launches": max(args.steps, 1)}), flush=True)
+                          "launches": max(args.steps, 1), "ms_per_copy": round(ms, 5),
+                          "GB/s_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}),
+              flush=True)
         return
 
     if args.decode:
