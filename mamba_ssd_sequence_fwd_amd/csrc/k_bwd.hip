@@ -279,6 +279,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
     sDt[t] = d;
     sCum[t] = d;
     sRow[t] = 0.f;
+    sDyx[t] = 0.f;  // tokens past the chunk end; the column tiles fill the rest
   }
   __syncthreads();
   wave0_scan<Q, false>(sCum);  // prefix sums of dt inside the chunk
@@ -295,20 +296,6 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
     }
   }
 
-  // dy . x per token (for dD), one token per thread.
-  for (int t = tid; t < Q; t += 256) {
-    float dyx = 0.f;
-    if (t < len) {
-#pragma unroll
-      for (int p0 = 0; p0 < kP; p0 += 8) {
-        const bf16x8 d8 = *reinterpret_cast<const bf16x8 *>(sDY + rswz<kP>(t, p0));
-        const bf16x8 x8 = ldg8(xs + (size_t)t * ldx + p0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dyx += (float)d8[e] * (float)x8[e];
-      }
-    }
-    sDyx[t] = dyx;
-  }
   __syncthreads();
 
   const float cs_last = sCs[len - 1];
@@ -332,6 +319,21 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
     }
 #pragma unroll
     for (int kp = 0; kp < kP / 32; ++kp) bX[kp] = ldg8_row(xs, ldx, s, len, 32 * kp + 8 * lg);
+    // dy_s . x_s (for dD) from the same x row: each lane has 16 of the 64 p,
+    // the four lanes of column s together all of them. x is read from HBM
+    // only here and in the epilogue just after, while the row is in cache.
+    {
+      float dyx = 0.f;
+#pragma unroll
+      for (int kp = 0; kp < kP / 32; ++kp) {
+        const bf16x8 d8 = *reinterpret_cast<const bf16x8 *>(sDY + rswz<kP>(s, 32 * kp + 8 * lg));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dyx += (float)d8[e] * (float)bX[kp][e];
+      }
+      dyx += __shfl_xor(dyx, 16);
+      dyx += __shfl_xor(dyx, 32);
+      if (lg == 0 && sv) sDyx[s] = dyx;
+    }
     f32x4 acc1[4], acc2[4], acc3[4];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
