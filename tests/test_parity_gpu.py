@@ -43,6 +43,11 @@ SMALL = {
     # kernel's three-per-CU variant (smaller grids take the deep-prefetch one)
     "many-units-N128": si.scaled(C[2], batch=2, seqlen=1800, nheads=52, seed=2026),
     "many-units-N64-h0": si.scaled(C[2], batch=4, seqlen=1000, nheads=64, dstate=64, seed=2027),
+    # 69 (sequence, head) pairs: the chained kernel's eight per-XCD ticket
+    # queues get 8 or 9 pairs each, so queues run dry at different times and
+    # workgroups take tickets from other XCDs' queues
+    "xcd-queues-uneven": si.scaled(C[2], batch=3, seqlen=700, nheads=23, h0_std=0.1,
+                                   seed=2028),
     "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
                               chunk=128, seed=2021),
     "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
