@@ -48,6 +48,9 @@ SMALL = {
     # workgroups take tickets from other XCDs' queues
     "xcd-queues-uneven": si.scaled(C[2], batch=3, seqlen=700, nheads=23, h0_std=0.1,
                                    seed=2028),
+    # 11 packed sequences, two of them empty, lengths from 1 to 900 tokens
+    "varlen-11-seqs": si.scaled(C[4], nheads=4, num_seqs=11, h0_std=0.1, seed=2029,
+                                seq_lens=(300, 0, 1, 700, 256, 257, 0, 40, 900, 5, 513)),
     "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
                               chunk=128, seed=2021),
     "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
