@@ -28,9 +28,8 @@
 //      C B^T tiles precomputed once per (chunk, group), plus 2^(cs_l) C_l h_in^T
 //      (the chunk_scan step); y.
 //
-// Tickets from an atomic counter (one per XCD on most dense problems, see
-// chain_xcd_queues) order the work units by chunk index inside the
-// sequence, then sequence, then head, so the predecessor of a unit took
+// Tickets from an atomic counter order the work units by chunk index inside
+// the sequence, then sequence, then head, so the predecessor of a unit took
 // its ticket a whole chunk-index level earlier and has normally published by
 // the time step 3 asks. A workgroup only ever waits on a smaller ticket, i.e.
 // on one that is already running, so the chain cannot deadlock whatever order
@@ -57,29 +56,6 @@ namespace ssd {
 constexpr float kLog2eChain = 1.4426950408889634f;
 constexpr int kChainWaves = 4;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// XCD-local work queues. The hardware deals workgroup b to XCD b mod 8, and
-// each XCD has an L2 of its own. With one global ticket counter the heads of
-// a chunk land on all eight XCDs, and each of their L2s fetches the chunk's
-// C rows, C B^T tiles and B^T tiles. With a queue per XCD (ints kXcdQueue0 +
-// q of the sync header), queue q owns the contiguous slice
-// [q ph / 8, (q + 1) ph / 8) of the ph = sequences x heads pairs, all chunks
-// of each, handed out by chunk index, so a chunk's heads share few L2s. A
-// workgroup takes a ticket from its own XCD's queue, and once that queue is
-// used up from the next ones in turn, so an XCD that runs ahead helps the
-// others. Every unit's predecessor sits in the same queue under a smaller
-// ticket, which a running workgroup holds, so the no-deadlock argument holds
-// per queue; the grid has exactly one workgroup per unit. Used for dense
-// problems with at least 8 pairs per queue and N <= 128. Interleaved A/B,
-// median of 8: the 2.7B shapes 183 -> 177 us, the config-1 shapes equal; at
-// N = 256 (two workgroups per CU) the long 16K-token shapes were 2.5% slower
-// (526 -> 539 us), so N = 256 keeps the single queue.
-constexpr int kXcds = 8;
-constexpr int kXcdQueue0 = 8;  // sync header ints [8, 16)
-
-__host__ __device__ inline bool chain_xcd_queues(const Args &a) {
-  return !a.varlen && a.N != 256 && a.nseq * a.H >= 8 * kXcds;
-}
 
 // Intra-chunk outputs of the 32-row tile i (rows 32i .. 32i+31), both 16-row
 // halves u, added into Y[u] (transposed: lane holds column l = 32i + 16u +
@@ -350,7 +326,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   __shared__ __attribute__((aligned(16))) float sU[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];
   __shared__ float sTot[4];
-  __shared__ int sTicket, sReady, sQueue;
+  __shared__ int sTicket, sReady;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -358,35 +334,12 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   int32_t *ticket = a.sync, *err = a.sync + 1, *pub = a.sync + kSyncHeader;
 
   // ---- 1. work unit, loads, decay tables -----------------------------------
-  const bool xq = chain_xcd_queues(a);
-  const int ph = a.nseq * a.H;
-  if (tid == 0) {
-    if (xq) {  // own XCD's queue first, then the others' leftovers
-      const int q0 = blockIdx.x & (kXcds - 1);
-      int t = -1, qq = q0;
-      for (int i = 0; i < kXcds && t < 0; ++i) {
-        qq = (q0 + i) & (kXcds - 1);
-        const int per = (qq + 1) * ph / kXcds - qq * ph / kXcds;
-        const int u = atomicAdd(a.sync + kXcdQueue0 + qq, 1);
-        if (u < per * a.nc_per) t = u;
-      }
-      sTicket = t;  // -1 cannot happen: the grid has one workgroup per unit
-      sQueue = qq;
-    } else {
-      sTicket = atomicAdd(ticket, 1);
-    }
-  }
+  if (tid == 0) sTicket = atomicAdd(ticket, 1);
   __syncthreads();
   const int tk = sTicket;
-  if (tk < 0) return;  // uniform per workgroup
   int c, h;
-  if (xq) {  // queue qq: pairs [lo, lo + per) of (sequence, head), by chunk index
-    const int qq = sQueue, lo = qq * ph / kXcds, per = (qq + 1) * ph / kXcds - lo;
-    const int j = tk / per, p = lo + tk - j * per, s = p / a.H;
-    h = p - s * a.H;
-    c = s * a.nc_per + j;
-  } else if (!a.varlen) {
-    const int per = ph;
+  if (!a.varlen) {
+    const int per = a.nseq * a.H;
     const int j = tk / per, r = tk - j * per, s = r / a.H;
     h = r - s * a.H;
     c = s * a.nc_per + j;

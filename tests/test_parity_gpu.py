@@ -43,11 +43,8 @@ SMALL = {
     # kernel's three-per-CU variant (smaller grids take the deep-prefetch one)
     "many-units-N128": si.scaled(C[2], batch=2, seqlen=1800, nheads=52, seed=2026),
     "many-units-N64-h0": si.scaled(C[2], batch=4, seqlen=1000, nheads=64, dstate=64, seed=2027),
-    # 69 (sequence, head) pairs: the chained kernel's eight per-XCD ticket
-    # queues get 8 or 9 pairs each, so queues run dry at different times and
-    # workgroups take tickets from other XCDs' queues
-    "xcd-queues-uneven": si.scaled(C[2], batch=3, seqlen=700, nheads=23, h0_std=0.1,
-                                   seed=2028),
+    # 69 (sequence, head) pairs, an odd head count, three ragged sequences
+    "odd-heads-23": si.scaled(C[2], batch=3, seqlen=700, nheads=23, h0_std=0.1, seed=2028),
     # 11 packed sequences, two of them empty, lengths from 1 to 900 tokens
     "varlen-11-seqs": si.scaled(C[4], nheads=4, num_seqs=11, h0_std=0.1, seed=2029,
                                 seq_lens=(300, 0, 1, 700, 256, 257, 0, 40, 900, 5, 513)),
