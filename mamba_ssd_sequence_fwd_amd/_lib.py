@@ -176,6 +176,20 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _same_device(dev, **tensors):
+    """Every tensor a kernel reads or writes must live on ``dev`` (the device
+    of the first input): a host pointer handed to a kernel would fault the GPU
+    instead of raising. Checked before anything is launched."""
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError("%s is on %s, but the other inputs are on %s" % (name, t.device, dev))
+
+
+def _on_gpu(dev):
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU (got %s)" % dev)
+
+
 class Plan:
     """A prepared ssd_forward call: validated problem, outputs and workspace
     allocated once; :meth:`run` only enqueues the kernels.
@@ -199,8 +213,9 @@ class Plan:
         batch, L, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
         dev = x.device
-        if dev.type != "cuda":
-            raise ValueError("tensors must be on the GPU (got %s)" % dev)
+        _same_device(dev, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state,
+                     dt_bias=dt_bias)
+        _on_gpu(dev)
         if x.dtype not in _DTYPES:
             raise ValueError("x must be bfloat16 or float32")
         for name, t, shape in (("dt", dt, (batch, L, H)), ("B", B, (batch, L, G, N)),
@@ -301,11 +316,28 @@ class Plan:
         w = self.workspace[lay.chain_sync:lay.chain_sync + 8].view(torch.int32)
         return int(w[1].item())
 
+    def check(self):
+        """Wait for the passes run so far and raise SSDError if the chained
+        kernel's error word is set (see :meth:`chain_error`)."""
+        err = self.chain_error()
+        if err:
+            raise SSDError(SSD_ERR_HIP, "ssd_forward",
+                           "a chained workgroup timed out waiting for its predecessor's "
+                           "state (error word %d); the outputs are invalid" % err)
+
 
 def forward(x, dt, A, B, C, D=None, initial_state=None, chunk_size=256, cu_seqlens=None,
-            **kw):
-    """SSD forward pass: returns (y, final_state)."""
-    return Plan(x, dt, A, B, C, D, initial_state, chunk_size, cu_seqlens, **kw).run()
+            *, check=False, **kw):
+    """SSD forward pass: returns (y, final_state).
+
+    With ``check=True`` the call waits for the pass and raises SSDError if a
+    chained workgroup gave up waiting for its predecessor's state (the error
+    word of the workspace; the outputs are then wrong)."""
+    plan = Plan(x, dt, A, B, C, D, initial_state, chunk_size, cu_seqlens, **kw)
+    y, hT = plan.run()
+    if check:
+        plan.check()
+    return y, hT
 
 
 def step(x, dt, A, B, C, D=None, state=None, *, y=None, stream=None):
@@ -323,8 +355,8 @@ def step(x, dt, A, B, C, D=None, state=None, *, y=None, stream=None):
         raise ValueError("B must be (batch, ngroups, dstate)")
     G, N = B.shape[1], B.shape[2]
     dev = x.device
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on the GPU (got %s)" % dev)
+    _same_device(dev, dt=dt, A=A, B=B, C=C, D=D, state=state, y=y)
+    _on_gpu(dev)
     if x.dtype not in _DTYPES:
         raise ValueError("x must be bfloat16 or float32")
     for name, t, shape in (("dt", dt, (batch, H)), ("B", B, (batch, G, N)),
@@ -347,8 +379,12 @@ def step(x, dt, A, B, C, D=None, state=None, *, y=None, stream=None):
     prob = make_problem(batch, 1, H, P, N, G, 0, 0, _DTYPES[x.dtype], 0)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    x, dt, A, B, C = (t.contiguous() for t in (x, dt, A, B, C))
-    D = D.contiguous() if D is not None else None
+    # copies of non-contiguous inputs are made on the stream the kernel runs
+    # on, so they are complete before it reads them and their memory is not
+    # reused before it has run
+    with torch.cuda.stream(stream):
+        x, dt, A, B, C = (t.contiguous() for t in (x, dt, A, B, C))
+        D = D.contiguous() if D is not None else None
     _check(load().ssd_step(ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                            _ptr(D), _ptr(state), _ptr(y), ctypes.c_void_p(stream.cuda_stream)),
            "ssd_step")
@@ -371,8 +407,9 @@ def selective_scan(x, delta, A, B, C, D=None, initial_state=None, *, want_final_
         raise ValueError("A must be (dim, dstate) float32")
     N = A.shape[1]
     dev = x.device
-    if dev.type != "cuda":
-        raise ValueError("tensors must be on the GPU (got %s)" % dev)
+    _same_device(dev, delta=delta, A=A, B=B, C=C, D=D, initial_state=initial_state, y=y,
+                 final_state=final_state)
+    _on_gpu(dev)
     if x.dtype not in _DTYPES:
         raise ValueError("x must be bfloat16 or float32")
     for name, t, shape in (("delta", delta, (batch, L, Dm)), ("B", B, (batch, L, N)),
@@ -385,15 +422,25 @@ def selective_scan(x, delta, A, B, C, D=None, initial_state=None, *, want_final_
                                       or initial_state.dtype != torch.float32):
         raise ValueError("initial_state must be (%d, %d, %d) float32" % (batch, Dm, N))
     prob = ScanProblem(batch, L, Dm, N, _DTYPES[x.dtype], 0)
-    x, delta, A, B, C = (t.contiguous() for t in (x, delta, A, B, C))
-    D = D.contiguous() if D is not None else None
-    h0 = initial_state.contiguous() if initial_state is not None else None
-    if y is None:
-        y = torch.empty_like(x)
-    if final_state is None and want_final_state:
-        final_state = torch.empty((batch, Dm, N), device=dev, dtype=torch.float32)
+    if y is not None and (tuple(y.shape) != (batch, L, Dm) or y.dtype != x.dtype
+                          or not y.is_contiguous()):
+        raise ValueError("y must be a contiguous (%d, %d, %d) %s tensor" % (batch, L, Dm, x.dtype))
+    if final_state is not None and (tuple(final_state.shape) != (batch, Dm, N)
+                                    or final_state.dtype != torch.float32
+                                    or not final_state.is_contiguous()):
+        raise ValueError("final_state must be a contiguous (%d, %d, %d) float32 tensor"
+                         % (batch, Dm, N))
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    # copies and outputs are made on the stream the kernel runs on (see step())
+    with torch.cuda.stream(stream):
+        x, delta, A, B, C = (t.contiguous() for t in (x, delta, A, B, C))
+        D = D.contiguous() if D is not None else None
+        h0 = initial_state.contiguous() if initial_state is not None else None
+        if y is None:
+            y = torch.empty_like(x)
+        if final_state is None and want_final_state:
+            final_state = torch.empty((batch, Dm, N), device=dev, dtype=torch.float32)
     _check(load().ssd_selective_scan(ctypes.byref(prob), _ptr(x), _ptr(delta), _ptr(A), _ptr(B),
                                      _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(final_state),
                                      ctypes.c_void_p(stream.cuda_stream)),
@@ -422,8 +469,9 @@ def conv1d_silu(xbc, weight, bias, x_dim, bc_dim, history=None, cu_seqlens=None,
     float32; history (sequences, K - 1, ch) in xbc's dtype or None. Outputs
     have xbc's leading shape with x_dim, bc_dim, bc_dim channels.
     """
-    if xbc.device.type != "cuda":
-        raise ValueError("tensors must be on the GPU (got %s)" % xbc.device)
+    _same_device(xbc.device, weight=weight, bias=bias, history=history, x=x, B=B, C=C,
+                 history_out=history_out)
+    _on_gpu(xbc.device)
     if xbc.dtype not in _DTYPES:
         raise ValueError("xbc must be bfloat16 or float32")
     ch = x_dim + 2 * bc_dim
@@ -460,20 +508,27 @@ def conv1d_silu(xbc, weight, bias, x_dim, bc_dim, history=None, cu_seqlens=None,
     hshape = (nseq, K - 1, ch)
     if history is not None and (tuple(history.shape) != hshape or history.dtype != xbc.dtype):
         raise ValueError("history must be %s %s" % (hshape, xbc.dtype))
-    weight = weight.contiguous()
-    bias = bias.contiguous() if bias is not None else None
-    history = history.contiguous() if history is not None else None
-    if x is None:
-        x = torch.empty(lead + (x_dim,), device=dev, dtype=xbc.dtype)
-    if B is None:
-        B = torch.empty(lead + (bc_dim,), device=dev, dtype=xbc.dtype)
-    if C is None:
-        C = torch.empty(lead + (bc_dim,), device=dev, dtype=xbc.dtype)
-    if history_out is None and want_history:
-        history_out = torch.empty(hshape, device=dev, dtype=xbc.dtype)
+    for name, t, shape in (("x", x, lead + (x_dim,)), ("B", B, lead + (bc_dim,)),
+                           ("C", C, lead + (bc_dim,)), ("history_out", history_out, hshape)):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != xbc.dtype
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous %s %s tensor" % (name, shape, xbc.dtype))
     prob = ConvProblem(batch, L, num_seqs, x_dim, bc_dim, K, in_stride, _DTYPES[xbc.dtype], 0)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
+    # copies and outputs are made on the stream the kernel runs on (see step())
+    with torch.cuda.stream(stream):
+        weight = weight.contiguous()
+        bias = bias.contiguous() if bias is not None else None
+        history = history.contiguous() if history is not None else None
+        if x is None:
+            x = torch.empty(lead + (x_dim,), device=dev, dtype=xbc.dtype)
+        if B is None:
+            B = torch.empty(lead + (bc_dim,), device=dev, dtype=xbc.dtype)
+        if C is None:
+            C = torch.empty(lead + (bc_dim,), device=dev, dtype=xbc.dtype)
+        if history_out is None and want_history:
+            history_out = torch.empty(hshape, device=dev, dtype=xbc.dtype)
     _check(load().ssd_conv1d_silu(ctypes.byref(prob), _ptr(xbc), _ptr(weight), _ptr(bias),
                                   _ptr(history), _ptr(cu_dev), _ptr(x), _ptr(B), _ptr(C),
                                   _ptr(history_out), ctypes.c_void_p(stream.cuda_stream)),
@@ -499,8 +554,9 @@ class BackwardPlan:
         batch, L, H, P = x.shape
         G, N = B.shape[2], B.shape[3]
         dev = x.device
-        if dev.type != "cuda":
-            raise ValueError("tensors must be on the GPU (got %s)" % dev)
+        _same_device(dev, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, dy=dy,
+                     dfinal_state=dfinal_state)
+        _on_gpu(dev)
         if x.dtype != torch.bfloat16:
             raise ValueError("the backward pass takes bfloat16 problems")
         for name, t, shape in (("dt", dt, (batch, L, H)), ("B", B, (batch, L, G, N)),

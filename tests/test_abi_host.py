@@ -364,3 +364,84 @@ def test_backward_workspace_size_and_checks(lib):
     ptrs = list(good)
     ptrs[17] = vp(4096 * 18 + 128)                  # workspace not 256-byte aligned
     assert _bwd_status(lib, prob, ptrs) == ssd.SSD_ERR_WORKSPACE
+
+
+# ---- the Python binding refuses tensors on another device ----------------------
+# Every tensor a kernel touches must sit on the device of the first input:
+# a host pointer handed to a kernel would fault the GPU instead of raising.
+# The check runs before the GPU check and before any launch, so it is
+# exercised here with inputs on torch's "meta" device and one tensor on the CPU.
+import torch  # noqa: E402
+
+
+def _meta(*shape, dtype=torch.bfloat16):
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+def _fwd_args(**over):
+    b, L, H, P, N, G = 2, 64, 4, 64, 128, 1
+    a = dict(x=_meta(b, L, H, P), dt=_meta(b, L, H), A=_meta(H, dtype=torch.float32),
+             B=_meta(b, L, G, N), C=_meta(b, L, G, N), D=_meta(H, dtype=torch.float32),
+             initial_state=_meta(b, H, P, N, dtype=torch.float32))
+    a.update(over)
+    return a
+
+
+@pytest.mark.parametrize("name,shape", [("A", (4,)), ("D", (4,)),
+                                        ("initial_state", (2, 4, 64, 128)),
+                                        ("dt", None), ("B", None)])
+def test_forward_rejects_tensor_on_another_device(name, shape):
+    a = _fwd_args()
+    a[name] = torch.zeros(shape or a[name].shape, dtype=a[name].dtype)   # on the CPU
+    with pytest.raises(ValueError, match=name):
+        ssd.Plan(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["initial_state"])
+
+
+def test_forward_on_meta_device_is_not_a_gpu():
+    a = _fwd_args()
+    with pytest.raises(ValueError, match="GPU"):
+        ssd.Plan(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["initial_state"])
+
+
+@pytest.mark.parametrize("name", ["A", "D", "state"])
+def test_step_rejects_tensor_on_another_device(name):
+    b, H, P, N = 3, 4, 64, 128
+    a = dict(x=_meta(b, H, P), dt=_meta(b, H), A=_meta(H, dtype=torch.float32),
+             B=_meta(b, 1, N), C=_meta(b, 1, N), D=_meta(H, dtype=torch.float32),
+             state=_meta(b, H, P, N, dtype=torch.float32))
+    a[name] = torch.zeros(a[name].shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        ssd.step(**a)
+
+
+@pytest.mark.parametrize("name", ["A", "D", "initial_state", "final_state"])
+def test_selective_scan_rejects_tensor_on_another_device(name):
+    b, L, Dm, N = 2, 16, 64, 16
+    a = dict(x=_meta(b, L, Dm), delta=_meta(b, L, Dm), A=_meta(Dm, N, dtype=torch.float32),
+             B=_meta(b, L, N), C=_meta(b, L, N), D=_meta(Dm, dtype=torch.float32),
+             initial_state=_meta(b, Dm, N, dtype=torch.float32),
+             final_state=_meta(b, Dm, N, dtype=torch.float32))
+    a[name] = torch.zeros(a[name].shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        ssd.selective_scan(**a)
+
+
+@pytest.mark.parametrize("name", ["A", "D", "initial_state", "dfinal_state"])
+def test_backward_rejects_tensor_on_another_device(name):
+    a = _fwd_args()
+    a["dy"] = _meta(*a["x"].shape)
+    a["dfinal_state"] = _meta(*a["initial_state"].shape, dtype=torch.float32)
+    a[name] = torch.zeros(a[name].shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        ssd.BackwardPlan(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["initial_state"],
+                         a["dy"], a["dfinal_state"])
+
+
+@pytest.mark.parametrize("name", ["weight", "bias", "history"])
+def test_conv_rejects_tensor_on_another_device(name):
+    ch = 64 + 2 * 16
+    a = dict(weight=_meta(ch, 4, dtype=torch.float32), bias=_meta(ch, dtype=torch.float32),
+             history=_meta(2, 3, ch))
+    a[name] = torch.zeros(a[name].shape, dtype=a[name].dtype)
+    with pytest.raises(ValueError, match=name):
+        ssd.conv1d_silu(_meta(2, 32, ch), a["weight"], a["bias"], 64, 16, a["history"])
