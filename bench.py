@@ -6,10 +6,12 @@ the path). Default workload: the 2.7B-shaped config (batch 8, L 2048, H 80,
 P 64, N 128, G 1, chunk 256, bf16 in / fp32 accumulate and states, random
 fp32 initial state). Inputs are resident in HBM before the timed region.
 
-Prints ONE JSON line with: whole-job tokens/s, the per-kernel times measured
-live with HIP events over the timed region, the roofline of the dominant
-kernel (algorithmic bytes or flops per launch / its mean event time), and the
-fp64 CPU oracle timed on this host (a reported baseline, not a target).
+Prints ONE JSON line with: whole-job tokens/s over K plain passes (HIP events
+around the loop only), per-kernel times from a second run of K passes with a
+HIP event after every kernel, the roofline of the dominant kernel (the
+method's algorithmic bytes or flops per launch / its mean event time, with
+the design's own intermediate bytes reported apart as overhead), and the fp64
+CPU oracle timed on this host (a reported baseline, not a target).
 
     python bench.py [--steps K] [--warmup W] [--config 0..4] [--no-cpu-baseline]
 """
@@ -68,11 +70,12 @@ def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
         bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + causal * G * 2 + S * H * state * (
             2 if inp["h0"] is not None else 1),
         flops=2 * causal * H * P + 4 * T * H * N * P + 2 * nc * H * P * N)
-    # chained kernel: the fused minimum plus the fp32 state hand-off between
-    # consecutive chunks of a sequence (written once, read once)
+    # chained kernel: the method's bytes are the fused minimum; the fp32 state
+    # hand-off between consecutive chunks of a sequence (written once, read
+    # once) is this design's own intermediate, reported apart as overhead
     handoff = 2 * (nc - S) * H * state
-    cost["ssd_chain"] = dict(bytes=cost["ssd_fused"]["bytes"] + handoff,
-                             flops=cost["ssd_fused"]["flops"])
+    cost["ssd_chain"] = dict(bytes=cost["ssd_fused"]["bytes"], flops=cost["ssd_fused"]["flops"],
+                             overhead_bytes=handoff)
     cost["_path"] = dict(
         bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + S * H * state * (
             2 if inp["h0"] is not None else 1),
@@ -517,35 +520,41 @@ def main():
                     chunk_size=w.chunk, cu_seqlens=inp["cu_seqlens"], unfused=args.unfused,
                     per_sequence=args.per_sequence)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        plan.run(stream)
-    torch.cuda.synchronize()
 
-    # Timed region: K steps, every kernel bracketed by HIP events on the
-    # stream the kernels run on; the call synchronises at the end.
-    t0 = time.perf_counter()
+    # Timed region (after W untimed warm-up passes): K plain ssd_forward passes (exactly what a caller
+    # enqueues), HIP events on the kernels' stream around the whole loop only,
+    # synchronised on both sides (or, with --cold, one pass at a time after an
+    # eviction read that the events do not cover).
+    ms_per_step, wall = time_launches(lambda: plan.run(stream), args, stream)
+    if plan.chain_error():
+        print("bench.py: a chained workgroup timed out waiting for its predecessor's state; "
+              "the outputs of the timed passes are invalid", file=sys.stderr)
+        sys.exit(3)
+    tokens = plan.tokens
+    value = tokens / (ms_per_step / 1e3)
+
+    # Per-kernel durations for the roofline, from a second run of K passes of
+    # the same launch sequence with a HIP event after every kernel (on the
+    # kernels' stream). Each figure is a kernel's duration plus its launch
+    # gap, so it can only understate the kernel's rate.
     if not args.cold:
-        times = plan.run_timed(args.steps, stream)
-        torch.cuda.synchronize()
-        per_kernel_ms = times.as_dict()
-        total_ms = per_kernel_ms.pop("_total_ms")
+        per_kernel_ms = plan.run_timed(args.steps, stream).as_dict()
+        per_kernel_ms.pop("_total_ms")
     else:
-        # One pass at a time, each after an eviction read that the events do
-        # not cover; per-kernel and total times are summed over passes.
         evict = torch.zeros(COLD_EVICT_BYTES // 4, device=dev, dtype=torch.float32)
-        per_kernel_ms, total_ms = {}, 0.0
+        per_kernel_ms = {}
         for i in range(args.steps):
             evict_caches(evict)
             t = plan.run_timed(1, stream).as_dict()
-            total_ms += t.pop("_total_ms")
+            t.pop("_total_ms")
             for k, v in t.items():
                 per_kernel_ms[k] = per_kernel_ms.get(k, 0.0) + v / args.steps
-        torch.cuda.synchronize()
         del evict
-    wall = time.perf_counter() - t0
-    ms_per_step = total_ms / args.steps
-    tokens = plan.tokens
-    value = tokens / (ms_per_step / 1e3)
+    torch.cuda.synchronize()
+    if plan.chain_error():
+        print("bench.py: a chained workgroup timed out in the per-kernel passes",
+              file=sys.stderr)
+        sys.exit(3)
 
     cost = algorithmic_cost(w, inp)
     kernels = {}
@@ -562,6 +571,8 @@ def main():
     roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(kd["GB/s"] / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom, w.name),
+                "alg_bytes": kd["alg_bytes"], "kernel_ms": kd["ms"],
+                "overhead_bytes": int(cost.get(dom, {}).get("overhead_bytes", 0)),
                 "mfma_frac": round(kd["TFLOP/s"] / (MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16"
                                                     else MFMA_FP32_PEAK_TFLOPS), 4)}
     path = cost["_path"]

@@ -83,3 +83,60 @@ def rel_err(a, b) -> float:
 
 def tol_of(inp: dict) -> float:
     return TOL[inp["workload"].dtype]
+
+
+def compare_every_pair(inp: dict, outs: dict, block_tokens: int = 16384):
+    """Compare GPU outputs with the oracle over EVERY (sequence, head) pair.
+
+    ``outs`` maps a label (a kernel path) to (y (T, H, P) tensor on the CPU,
+    final_state (S, H, P, N) tensor on the CPU). The oracle runs once, over
+    blocks of whole sequences of about ``block_tokens`` tokens, and every
+    label is compared against the same reference. Returns per label a dict:
+    normwise errors of y and of the final state over the whole tensor
+    (max|gpu - ref| / max|ref|), the worst per-(sequence, head) slice error
+    of each (the same ratio within the slice), and the pair it occurs at.
+    """
+    x, dt, B, C = flat_inputs(inp)
+    lens = seq_lens_of(inp)
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    H = x.shape[1]
+    f = oracle._np
+    acc = {k: dict(dy=0.0, ry=0.0, dh=0.0, rh=0.0, wy=0.0, wy_at=None, wh=0.0, wh_at=None)
+           for k in outs}
+    s0 = 0
+    while s0 < len(lens):
+        s1, tok = s0, 0
+        while s1 < len(lens) and (s1 == s0 or tok + lens[s1] <= block_tokens):
+            tok += lens[s1]
+            s1 += 1
+        a, b = int(starts[s0]), int(starts[s1])
+        h0 = None if inp["h0"] is None else f(inp["h0"][s0:s1])
+        yr, hr = oracle.ssd_recurrence(f(x[a:b]), f(dt[a:b]), f(inp["A"]), f(B[a:b]), f(C[a:b]),
+                                       f(inp["D"]), h0, lens[s0:s1])
+        for k, (y, hT) in outs.items():
+            r = acc[k]
+            yg = y[a:b].to(torch.float64).numpy()
+            hg = hT[s0:s1].to(torch.float64).numpy()
+            dy = np.abs(yg - yr)
+            dh = np.abs(hg - hr)
+            r["dy"] = max(r["dy"], float(dy.max()) if dy.size else 0.0)
+            r["ry"] = max(r["ry"], float(np.abs(yr).max()) if yr.size else 0.0)
+            r["dh"] = max(r["dh"], float(dh.max()))
+            r["rh"] = max(r["rh"], float(np.abs(hr).max()))
+            for j in range(s1 - s0):
+                ja, jb = int(starts[s0 + j]) - a, int(starts[s0 + j + 1]) - a
+                for h in range(H):
+                    if jb > ja:
+                        e = float(dy[ja:jb, h].max()) / max(float(np.abs(yr[ja:jb, h]).max()), 1e-30)
+                        if e > r["wy"]:
+                            r["wy"], r["wy_at"] = e, (s0 + j, h)
+                    e = float(dh[j, h].max()) / max(float(np.abs(hr[j, h]).max()), 1e-30)
+                    if e > r["wh"]:
+                        r["wh"], r["wh_at"] = e, (s0 + j, h)
+        s0 = s1
+    res = {}
+    for k, r in acc.items():
+        res[k] = dict(y=r["dy"] / max(r["ry"], 1e-30), final=r["dh"] / max(r["rh"], 1e-30),
+                      worst_y=r["wy"], worst_y_at=r["wy_at"], worst_final=r["wh"],
+                      worst_final_at=r["wh_at"], pairs=len(lens) * H)
+    return res
