@@ -218,6 +218,10 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
   __shared__ __attribute__((aligned(16))) bf16 sG[kP * N];
   __shared__ __attribute__((aligned(16))) bf16 sHin[kP * N];
   __shared__ float sCs[Q], sDt[Q], sCum[Q], sDd[Q], sRow[Q], sCol[Q], sE[Q], sV[Q], sDyx[Q];
+  // row sums of W, one partial per wave (each wave adds its column tiles in a
+  // fixed order; the four partials are then added in wave order), so that
+  // dx, ddt and dA do not depend on the order the waves run in
+  __shared__ float sRowW[4][Q];
   __shared__ float sRed[4];
   Chunk k;
   const int c = blockIdx.x;
@@ -278,7 +282,8 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
                             : 0.f;
     sDt[t] = d;
     sCum[t] = d;
-    sRow[t] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sRowW[w][t] = 0.f;
     sDyx[t] = 0.f;  // tokens past the chunk end; the column tiles fill the rest
   }
   __syncthreads();
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
         // lane bits (b0, b1, b2) select value index 4 b0 + 2 b1 + b2
         const int e = 4 * b0 + 2 * b1 + b2;
         const int l = l0 + 16 * (e / 4) + 4 * lg + (e % 4);
-        if ((lr >> 3) == 0 && l < len) atomicAdd(&sRow[l], v1);
+        if ((lr >> 3) == 0 && l < len) sRowW[wave][l] += v1;
       }
     }
     colp += __shfl_xor(colp, 16);
@@ -460,9 +465,10 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
   for (int t = tid; t < len; t += 256) esum += sE[t];
   const float K = exp2_fast(cs_last) * block_sum(ghin, sRed) + block_sum(esum, sRed);
 
-  // dL_t into sRow (reusing it), and a copy for the suffix sums (in sCol)
+  // dL_t into sRow, and a copy for the suffix sums (in sCol)
   for (int t = tid; t < Q; t += 256) {
-    const float d = t < len ? sRow[t] - sCol[t] + sV[t] - sE[t] + (t == len - 1 ? K : 0.f) : 0.f;
+    const float row = ((sRowW[0][t] + sRowW[1][t]) + sRowW[2][t]) + sRowW[3][t];
+    const float d = t < len ? row - sCol[t] + sV[t] - sE[t] + (t == len - 1 ? K : 0.f) : 0.f;
     sRow[t] = d;
     sCol[t] = d;
   }

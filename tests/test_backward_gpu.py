@@ -149,3 +149,21 @@ def test_backward_full_workload_sampled():
         got = float(np.sum(g[gk].double().cpu().numpy().reshape(shape) * val))
         print("  <d%s, %s> %.6e vs %.6e" % (name, name, got, want), flush=True)
         assert abs(got - want) <= TOL["bf16"] * abs(want), (name, got, want)
+
+
+def test_backward_is_deterministic():
+    """Every gradient is bit-identical across repeated passes: the kernels sum
+    in a fixed order (no float atomics), whatever order their waves run in."""
+    w = si.scaled(BASE, batch=2, seqlen=1024, nheads=16, seed=5050)
+    inp = si.make_inputs(w)
+    gin = si.make_grad_inputs(w, inp)
+    d = {k: (None if inp[k] is None else inp[k].cuda()) for k in ("x", "dt", "A", "B", "C", "D", "h0")}
+    plan = ssd.BackwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                            gin["dy"].cuda(), gin["dhT"].cuda(), w.chunk)
+    print("[gpu] backward determinism %r" % plan.prob, flush=True)
+    first = {k: v.clone() for k, v in plan.run().items()}
+    for _ in range(4):
+        again = plan.run()
+        torch.cuda.synchronize()
+        for k, v in first.items():
+            assert torch.equal(v, again[k]), k
