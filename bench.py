@@ -39,12 +39,14 @@ COLD_EVICT_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
 MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
-def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
+def algorithmic_cost(w: si.Workload, inp: dict, chunks_per_unit: int = 1) -> dict:
     """Bytes each kernel must move and flops it must do, by the method's
     definition (unique HBM bytes; causal pairs only; C B^T once per group).
 
     Per (chunk, head) unit with q tokens: x q*P*e, y q*P*e, dt q*e, state
     P*N*4 (fp32), cumsum q*4; per (chunk, group): B and C q*N*e each.
+    ``chunks_per_unit``: consecutive chunks the chained kernel's workgroups
+    walk with the state on chip (the hand-off overhead is between units).
     """
     e = 2 if w.dtype == "bf16" else 4
     lens = inp["seq_lens"] or [w.seqlen] * w.batch
@@ -73,9 +75,16 @@ def algorithmic_cost(w: si.Workload, inp: dict) -> dict:
     # chained kernel: the method's bytes are the fused minimum; the fp32 state
     # hand-off between consecutive chunks of a sequence (written once, read
     # once) is this design's own intermediate, reported apart as overhead
-    handoff = 2 * (nc - S) * H * state
+    k = max(1, chunks_per_unit)
+    units = sum(((L + Q - 1) // Q + k - 1) // k for L in lens)
+    handoff = 2 * (units - sum(1 for L in lens if L > 0)) * H * state
     cost["ssd_chain"] = dict(bytes=cost["ssd_fused"]["bytes"], flops=cost["ssd_fused"]["flops"],
                              overhead_bytes=handoff)
+    # fp32 problems: one workgroup per (sequence, head), no C B^T tiles
+    cost["ssd_f32seq"] = dict(
+        bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + S * H * state * (
+            2 if inp["h0"] is not None else 1),
+        flops=2 * causal * (G * N + H * P) + 4 * T * H * N * P + 2 * nc * H * P * N)
     cost["_path"] = dict(
         bytes=2 * T * H * P * e + T * H * e + 2 * T * G * N * e + S * H * state * (
             2 if inp["h0"] is not None else 1),
@@ -556,7 +565,7 @@ def main():
               file=sys.stderr)
         sys.exit(3)
 
-    cost = algorithmic_cost(w, inp)
+    cost = algorithmic_cost(w, inp, int(plan.layout().chain_chunks_per_unit))
     kernels = {}
     for name, ms in per_kernel_ms.items():
         c = cost.get(name, {"bytes": 0, "flops": 0})

@@ -147,6 +147,13 @@ ssd_status ssd_workspace_size(const ssd_problem *prob, size_t *bytes);
  *   stream         a hipStream_t (NULL = the default stream)
  * Inputs and outputs must not overlap. Returns SSD_OK once all kernels are
  * enqueued; SSD_ERR_HIP if a launch fails.
+ * The chained kernel (the default for bf16) bounds each of its waits for a
+ * predecessor's state by one second; a wait that runs out sets the int32
+ * error word chain_sync[1] of the workspace (ssd_get_workspace_layout) and
+ * that pass's y and final_state are wrong. The word is cleared at the start
+ * of every pass; a caller that must know reads it after the stream has
+ * completed (no kernel of this library ever waits on another stream, so the
+ * bound is only reached if the device stalls).
  */
 ssd_status ssd_forward(const ssd_problem *prob, const void *x, const void *dt,
                        const float *A, const void *B, const void *C,
@@ -220,6 +227,11 @@ typedef struct ssd_workspace_layout {
                                gave up waiting for its predecessor's state
                                (outputs then wrong); 0 = no chained kernel */
   int64_t chain_sync_words; /* number of those words (0 = none) */
+  int64_t chain_chunks_per_unit; /* consecutive chunks of one (sequence, head)
+                               that one workgroup of the chained kernel walks,
+                               passing the state between them on chip; the
+                               state goes through the workspace only between
+                               such units (0 = no chained kernel) */
 } ssd_workspace_layout;
 ssd_status ssd_get_workspace_layout(const ssd_problem *prob,
                                     ssd_workspace_layout *layout);

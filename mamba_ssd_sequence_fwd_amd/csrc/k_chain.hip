@@ -28,6 +28,11 @@
 //      C B^T tiles precomputed once per (chunk, group), plus 2^(cs_l) C_l h_in^T
 //      (the chunk_scan step); y.
 //
+// For dense problems with more units than the chip holds, a work unit is a
+// segment of two consecutive chunks of one (sequence, head), walked by one
+// workgroup with the state passed between them in registers (kSeg below), so
+// only every second chunk boundary goes through the ring.
+//
 // Tickets from an atomic counter order the work units by chunk index inside
 // the sequence, then sequence, then head, so the predecessor of a unit took
 // its ticket a whole chunk-index level earlier and has normally published by
@@ -48,7 +53,7 @@
 // arithmetic (LDS returns in order).
 //
 // HBM traffic: x, y once; B, C, dt and the C B^T tiles once per head
-// through L2; 32 KB of fp32 state written and read per (chunk, head).
+// through L2; 32 KB of fp32 state written and read per (work unit, head).
 #include "mfma_common.h"
 
 namespace ssd {
@@ -310,15 +315,25 @@ __device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, c
 // 66 -> 56 us); with many units per slot the third workgroup per CU hides
 // that latency better (the 2.7B shapes: equal; long packed input: 13%
 // slower), so the launcher picks it by grid size.
-template <int N, int Q, bool kDeep>
+//
+// kSeg: a work unit is a segment of up to a.seg consecutive chunks of one
+// (sequence, head), walked in order by the same workgroup. Inside a segment
+// the state passes from chunk to chunk in registers (it is carried through
+// the output phase of the chunk before), so only the segment's last chunk
+// writes the ring and only its first reads it: a segment of k chunks moves
+// 1/k of the hand-off bytes of k one-chunk units. The carried state costs 32
+// registers (N = 128), so segments run two workgroups per CU.
+template <int N, int Q, bool kDeep, bool kSeg>
 __global__ __launch_bounds__(64 * kChainWaves)
-__attribute__((amdgpu_waves_per_eu(N == 256 || kDeep ? 2 : 3, N == 256 || kDeep ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(N == 256 || kDeep || kSeg ? 2 : 3,
+                                   N == 256 || kDeep || kSeg ? 2 : 3)))
 void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   constexpr int T = Q / 32, PAIRS = T * (T + 1) / 2, NKS = Q / 32;
   constexpr int NTW = N / 64;                 // 16-row n tiles of the state per wave
   constexpr int NTILE = T == 8 ? 2 : 1;       // 32-row output tiles per wave
   static_assert(Q == 128 || Q == 256, "chain kernel: chunk 128 or 256");
   static_assert(N == 64 || N == 128 || N == 256, "chain kernel: N 64, 128 or 256");
+  static_assert(!kSeg || N != 256, "chain kernel: no segments at N = 256 (registers)");
   __shared__ __attribute__((aligned(16))) bf16 sX[Q * kP];  // x, [token][p]
   __shared__ __attribute__((aligned(16))) bf16 sH[kP * N];  // h_in (bf16), [p][n]
   __shared__ __attribute__((aligned(16))) float sCs[Q];
@@ -328,33 +343,53 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   __shared__ float sTot[4];
   __shared__ int sTicket, sReady;
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
   int32_t *ticket = a.sync, *err = a.sync + 1, *pub = a.sync + kSyncHeader;
 
-  // ---- 1. work unit, loads, decay tables -----------------------------------
+  // ---- work unit: (first chunk, head, chunks in the segment) -----------------
   if (tid == 0) sTicket = atomicAdd(ticket, 1);
   __syncthreads();
   const int tk = sTicket;
-  int c, h;
+  int c0, h, nk = 1;
   if (!a.varlen) {
     const int per = a.nseq * a.H;
     const int j = tk / per, r = tk - j * per, s = r / a.H;
     h = r - s * a.H;
-    c = s * a.nc_per + j;
-  } else {  // chunk order of the plan (by index inside the sequence)
+    const int i0 = kSeg ? j * a.seg : j;
+    c0 = s * a.nc_per + i0;
+    if (kSeg) nk = min(a.seg, a.nc_per - i0);
+  } else {  // segment order of the plan (by segment index inside the sequence)
     const int kk = tk / a.H;
     h = tk - kk * a.H;
-    if (kk >= a.plan[0]) return;  // unused chunk slot: uniform per workgroup
-    c = a.plan[a.order_off + kk];
+    if (kk >= a.plan[kSeg ? a.nseg_off : 0]) return;  // unused slot: uniform per workgroup
+    c0 = a.plan[a.order_off + kk];
   }
-  Chunk k;
-  if (!chunk_of(a, c, k)) return;
+  if (kSeg && a.varlen) {
+    Chunk k0;
+    if (!chunk_of(a, c0, k0)) return;
+    int q0, q1;
+    chunks_of_seq(a, k0.seq, q0, q1);
+    nk = min(a.seg, q1 - c0);
+  }
   const int g = h / a.heads_per_group;
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N, PN = (size_t)kP * N;
+  f32x4 hcarry[NTW][4];  // kSeg: the state leaving the previous chunk of the segment
+
+  // One chunk of the work unit; `tid` is passed in so that a segment's loop
+  // recomputes the lane-derived offsets per chunk instead of keeping them
+  // live (in registers) across the whole walk.
+  auto chunk_body = [&](const int ci, const int tid) -> bool {
+  const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int c = c0 + ci;
+  Chunk k;
+  if (!chunk_of(a, c, k)) return false;
+  if (kSeg && ci > 0) __syncthreads();  // the previous chunk's outputs have read LDS
+  const bool head = !kSeg || ci == 0;   // first chunk of the work unit
+  const bool tail = !kSeg || ci == nk - 1;  // last chunk of the work unit
   const bf16 *xc = static_cast<const bf16 *>(a.x) + (size_t)k.start * ldx + (size_t)h * kP;
   const bf16 *cc = static_cast<const bf16 *>(a.C) + (size_t)k.start * ldb + (size_t)g * N;
+  // ---- 1. loads, decay tables ------------------------------------------------
   // Loads in the order they are needed (vector memory loads complete in
   // issue order): dt, the predecessor poll, the first B^T tiles, then x into
   // registers, one instruction per 32-token step (instruction k of wave w:
@@ -369,7 +404,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   const int pair = k.seq * a.H + h;
   const bool first = k.idx == 0;
   int early = 0;  // published count of the predecessor, read early
-  if (!first && tid == 0)
+  if (head && !first && tid == 0)
     early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float ah = a.A[h] * kLog2eChain;
   const float dsk = a.D ? a.D[h] : 0.f;
@@ -402,7 +437,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   };
   const float incl = wave_inclusive_sum(dtv * ah);
   if (lane == 63 && wave < Q / 64) sTot[wave] = incl;
-  if (tid == 0) sReady = (first || early >= k.idx) ? 1 : 0;
+  if (head && tid == 0) sReady = (first || early >= k.idx) ? 1 : 0;
   __syncthreads();
   float pre = 0.f, cs_last = 0.f;
 #pragma unroll
@@ -411,7 +446,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     pre += w < wave ? t : 0.f;
     cs_last += t;
   }
-  const bool ready = sReady != 0;
+  const bool ready = !head || sReady != 0;
   const float cst = incl + pre;
   const float cs_tile_end = __shfl(cst, lane | 31);
   if (tid < Q) {
@@ -427,7 +462,14 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
 
   // ---- 2. S_c = (w o B)^T x; h_in loads in flight when already published ------
   f32x4 hin[NTW][4];
-  if (ready) load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
+  if (!head) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hin[j][pt] = hcarry[j][pt];
+  } else if (ready) {
+    load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
+  }
   f32x4 hs[NTW][4];
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
@@ -475,7 +517,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   }
 
   // ---- 3. h_in; h_out = 2^(cs_last) h_in + S_c to the ring; publish ------------
-  const int iA = T == 8 ? wave : wave, iB = T - 1 - wave;
+  const int iA = wave, iB = T - 1 - wave;
   bf16x8 acA[2][N / 32];
   load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);  // used after the hand-off
   if (!ready) {
@@ -495,7 +537,9 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     for (int pt = 0; pt < 4; ++pt) {
       const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
       const f32x4 hout = dec * hin[j][pt] + hs[j][pt];
-      if (!last) {
+      if (!tail) {
+        hcarry[j][pt] = hout;  // the next chunk of the segment starts from it
+      } else if (!last) {
         ring_store4(rout, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16), hout);
       } else if (a.hT) {
         *reinterpret_cast<float4 *>(a.hT + (size_t)pair * PN + (size_t)p * N + n) =
@@ -506,9 +550,9 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
       hb.y = pack2(hin[j][pt][2], hin[j][pt][3]);
       *reinterpret_cast<uint2 *>(sH + swz<N>(p, n)) = hb;
     }
-  wait_vmem_all();  // this wave's ring stores have completed (device-coherent)
+  if (tail) wait_vmem_all();  // this wave's ring stores have completed (device-coherent)
   __syncthreads();  // ... and every other wave's; sH complete
-  if (!last && tid == 0)
+  if (tail && !last && tid == 0)
     __hip_atomic_store(pub + pair, k.idx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- 4. outputs, one 32-row tile at a time ------------------------------------
@@ -527,6 +571,19 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     state_tile<N>(iB, Y, sH, sCs, acB, k.len, lane);
     intra_tile<Q>(iB, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
     store_tile(iB, Y, k.len, yc, ldx, lane);
+  }
+  return true;
+  };  // chunk_body
+
+  if constexpr (kSeg) {
+#pragma unroll 1
+    for (int ci = 0; ci < nk; ++ci) {
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      if (!chunk_body(ci, t)) break;
+    }
+  } else {
+    chunk_body(0, tid);
   }
 }
 
@@ -559,21 +616,50 @@ bool chain_path_supports(const Args &a) {
 // at three workgroups each.
 constexpr int64_t kDeepMaxUnits = 3 * 256;
 
+// Chunks per work unit for problems with more units than the chip holds at
+// once. Order-balanced A/B, same box: the 2.7B-shaped workload 186.5 -> 174.2
+// us per pass with segments of 2 (4: 173.6; 8: 199.3), the long packed one
+// 1687 -> 1816 us (4: 1727). The packed workload is the more sensitive to the
+// third workgroup per CU that segments give up, so packed input keeps
+// one-chunk units.
+constexpr int kChainSeg = 2;
+
+int chain_segment(const Args &a) {
+  if (a.N == 256 || a.varlen) return 1;
+  // one-chunk units when they all fit the chip at once: there each unit's
+  // latency is the whole time, and a longer chain of dependent links within a
+  // workgroup would only lengthen it
+  if ((int64_t)a.nc_max * a.H <= kDeepMaxUnits) return 1;
+  return kChainSeg;
+}
+
+int64_t chain_units(const Args &a) {
+  const int s = a.seg;
+  if (!a.varlen) return (int64_t)a.nseq * ((a.nc_per + s - 1) / s) * a.H;
+  // sum over sequences of ceil(chunks / s) <= (chunks + sequences (s - 1)) / s
+  return (((int64_t)a.nc_max + (int64_t)a.nseq * (s - 1)) / s) * a.H;
+}
+
 template <int N, int Q>
 static hipError_t launch_chain_nq(const Args &a, const void *cb, const void *bt,
                                   hipStream_t st) {
-  const int64_t blocks = (int64_t)a.nc_max * a.H;
+  const int64_t blocks = chain_units(a);
   if (blocks == 0) return hipSuccess;
   const bf16 *cbp = static_cast<const bf16 *>(cb), *btp = static_cast<const bf16 *>(bt);
-  if constexpr (N != 256) {  // at N = 256 the deep variant does not fit the registers
+  if constexpr (N != 256) {  // at N = 256 neither variant fits the registers
+    if (a.seg > 1) {
+      hipLaunchKernelGGL((k_ssd_chain<N, Q, false, true>), dim3((unsigned)blocks),
+                         dim3(64 * kChainWaves), 0, st, a, cbp, btp);
+      return hipGetLastError();
+    }
     if (blocks <= kDeepMaxUnits) {
-      hipLaunchKernelGGL((k_ssd_chain<N, Q, true>), dim3((unsigned)blocks),
+      hipLaunchKernelGGL((k_ssd_chain<N, Q, true, false>), dim3((unsigned)blocks),
                          dim3(64 * kChainWaves), 0, st, a, cbp, btp);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((k_ssd_chain<N, Q, false>), dim3((unsigned)blocks), dim3(64 * kChainWaves),
-                     0, st, a, cbp, btp);
+  hipLaunchKernelGGL((k_ssd_chain<N, Q, false, false>), dim3((unsigned)blocks),
+                     dim3(64 * kChainWaves), 0, st, a, cbp, btp);
   return hipGetLastError();
 }
 

@@ -13,7 +13,6 @@
 namespace ssd {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kOrderMaxSeqs = 4096;
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   __shared__ int s_wave_tot[kPlanThreads / 64];
@@ -56,6 +55,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
     a.plan[0] = bad ? 0 : carry;
     a.plan[1] = bad ? 1 : 0;
     first[S] = bad ? 0 : carry;
+    if (bad) a.plan[a.nseg_off] = 0;  // no chained work units either
   }
   if (bad) return;
   for (int s = tid; s < S; s += kPlanThreads) {
@@ -63,22 +63,37 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
     for (int i = 0, off = 0; off < len; ++i, off += Q)
       rec[c0 + i] = make_int4(s, lo + off, min(Q, len - off), i);
   }
-  // Chunk order for the chained kernel: by index inside the sequence, then
-  // by sequence (all first chunks, then all second chunks, ...), so that a
-  // chunk comes long after its predecessor. Chunk i of sequence s goes to
-  // position sum_s' min(chunks(s'), i) + #{s' < s : chunks(s') > i}; with
-  // more than kOrderMaxSeqs sequences the sequence-major order is kept.
+  // Work-unit order for the chained kernel. A unit is a segment of up to
+  // a.seg consecutive chunks of one sequence (a.seg = 1: one chunk), and the
+  // list holds each segment's first chunk: by segment index inside the
+  // sequence, then by sequence (all first segments, then all second ones,
+  // ...), so that a segment comes long after its predecessor. Segment j of
+  // sequence s goes to position sum_s' min(segs(s'), j) + #{s' < s : segs(s')
+  // > j}. With more than kOrderMaxSeqs sequences (the host then uses one-chunk
+  // units) the sequence-major chunk order is kept.
   int *order = a.plan + a.order_off;
   const int nc = carry;
+  const int seg = max(a.seg, 1);
   if (S > kOrderMaxSeqs) {
     for (int c = tid; c < nc; c += kPlanThreads) order[c] = c;
+    if (tid == 0) a.plan[a.nseg_off] = nc;
     return;
   }
+  int nseg_part = 0;
   for (int s = tid; s < S; s += kPlanThreads) {
     s_first[s] = first[s];
     s_nch[s] = (a.cu[s + 1] - a.cu[s] + Q - 1) / Q;
+    nseg_part += (s_nch[s] + seg - 1) / seg;
   }
+  // total number of segments: wave sums, then one thread adds the waves
+  nseg_part = wave_inclusive_sum(nseg_part);
+  if (lane == 63) s_wave_tot[wave] = nseg_part;
   __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int w = 0; w < kPlanThreads / 64; ++w) tot += s_wave_tot[w];
+    a.plan[a.nseg_off] = tot;
+  }
   for (int c = tid; c < nc; c += kPlanThreads) {
     int lo = 0, hi = S - 1;  // last sequence whose first chunk is <= c
     while (lo < hi) {
@@ -87,10 +102,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
       else hi = mid - 1;
     }
     const int i = c - s_first[lo];
+    if (i % seg != 0) continue;  // not the first chunk of a segment
+    const int j = i / seg;
     int pos = 0;
     for (int s2 = 0; s2 < S; ++s2) {
-      const int n2 = s_nch[s2];
-      pos += min(n2, i) + ((s2 < lo && n2 > i) ? 1 : 0);
+      const int n2 = (s_nch[s2] + seg - 1) / seg;
+      pos += min(n2, j) + ((s2 < lo && n2 > j) ? 1 : 0);
     }
     order[pos] = c;
   }

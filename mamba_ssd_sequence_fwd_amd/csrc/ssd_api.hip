@@ -52,6 +52,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Which kernels a problem runs on.
 enum Path {
+  kF32Seq,       // fp32: one workgroup per (sequence, head) on fp32 MFMA, one launch
   kGeneric,      // plain FMA chunk kernels (fp32, and shapes MFMA does not cover)
   kMfmaUnfused,  // one MFMA kernel per step of the method
   kMfmaFused,    // C B^T per (chunk, group) + one fused kernel per (sequence, head)
@@ -68,11 +69,14 @@ struct Layout {
 };
 
 Path path_of(const ssd_problem &p) {
-  if (p.dtype != SSD_DTYPE_BF16 || (p.flags & SSD_FLAG_GENERIC_KERNELS)) return kGeneric;
   ssd::Args a{};
   a.P = p.headdim;
   a.N = p.dstate;
   a.Q = p.chunk_size;
+  if (p.dtype == SSD_DTYPE_F32 && !(p.flags & (SSD_FLAG_GENERIC_KERNELS | SSD_FLAG_UNFUSED)) &&
+      ssd::f32seq_path_supports(a))
+    return kF32Seq;
+  if (p.dtype != SSD_DTYPE_BF16 || (p.flags & SSD_FLAG_GENERIC_KERNELS)) return kGeneric;
   if (!ssd::mfma_path_supports(a)) return kGeneric;
   if (p.flags & SSD_FLAG_UNFUSED) return kMfmaUnfused;
   if (p.flags & SSD_FLAG_PER_SEQUENCE)
@@ -85,11 +89,12 @@ Layout make_layout(const ssd_problem &p) {
   const int64_t Q = p.chunk_size;
   L.nc_max = p.num_seqs > 0 ? p.seqlen / Q + p.num_seqs
                             : (int64_t)p.batch * ((p.seqlen + Q - 1) / Q);
-  L.rec_off = p.num_seqs > 0 ? (int64_t)round_up(3 + (size_t)p.num_seqs, 4) : 0;
-  // varlen: header, first chunk per sequence, 4-int records, chunk order
+  L.rec_off = p.num_seqs > 0 ? (int64_t)round_up(4 + (size_t)p.num_seqs, 4) : 0;
+  // varlen: header, first chunk per sequence and the total, the number of
+  // chained work units, 4-int records, work-unit order
   const size_t plan_ints = p.num_seqs > 0 ? (size_t)(L.rec_off + 5 * L.nc_max) : 4;
   L.path = path_of(p);
-  L.mfma = L.path != kGeneric;
+  L.mfma = L.path != kGeneric && L.path != kF32Seq;
   const bool unfused = L.path == kGeneric || L.path == kMfmaUnfused;  // per-chunk intermediates
   size_t off = 0;
   L.plan = off;
@@ -190,6 +195,8 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.heads_per_group = p->nheads / p->ngroups;
   a.rec_off = (int32_t)L.rec_off;
   a.order_off = (int32_t)(L.rec_off + 4 * L.nc_max);
+  a.nseg_off = varlen ? 3 + p->num_seqs : 0;
+  a.seg = L.path == kMfmaChain ? ssd::chain_segment(a) : 1;
   return a;
 }
 
@@ -208,6 +215,10 @@ struct StageNames {
 StageNames stage_names(const ssd::Args &a, const Layout &L, bool) {
   StageNames n{};
   if (a.varlen) n.name[n.count++] = "plan";
+  if (L.path == kF32Seq) {
+    n.name[n.count++] = "ssd_f32seq";
+    return n;
+  }
   if (L.path == kMfmaFused) {
     if (a.nc_max > 0) n.name[n.count++] = "chunk_cb";
     n.name[n.count++] = "ssd_fused";
@@ -250,6 +261,10 @@ ssd_status enqueue(const ssd::Args &a, const Layout &L, bool bf, hipStream_t s,
   } while (0)
   if (!mark()) return fail(SSD_ERR_HIP, "hipEventRecord failed");
   if (a.varlen) SSD_LAUNCH(ssd::launch_plan(a, s), "plan");
+  if (L.path == kF32Seq) {
+    SSD_LAUNCH(ssd::launch_f32seq(a, s), "ssd_f32seq");
+    return SSD_OK;
+  }
   if (L.path == kMfmaFused) {
     if (a.nc_max > 0) SSD_LAUNCH(ssd::launch_chunk_cb(a, a.cb, s), "chunk_cb");
     SSD_LAUNCH(ssd::launch_fused(a, a.cb, a.zeros, s), "ssd_fused");
@@ -533,6 +548,15 @@ ssd_status ssd_get_workspace_layout(const ssd_problem *p, ssd_workspace_layout *
   out->max_chunks = L.nc_max;
   out->chain_sync = L.nsync ? L.sync : 0;
   out->chain_sync_words = L.nsync;
+  out->chain_chunks_per_unit = 0;
+  if (L.nsync) {
+    ssd::Args a{};
+    a.N = p->dstate;
+    a.H = p->nheads;
+    a.varlen = p->num_seqs > 0 ? 1 : 0;
+    a.nc_max = (int32_t)L.nc_max;
+    out->chain_chunks_per_unit = ssd::chain_segment(a);
+  }
   return SSD_OK;
 }
 

@@ -42,10 +42,17 @@ struct Args {
   int32_t order_off;    // int offset of the chunk order (by index in sequence) inside plan
   const float *dt_bias; // (H) or null: per-head offset of the step pre-activation
   int32_t dt_softplus;  // 0: dt is the step; 1: dt is its pre-activation
+  int32_t seg;          // chain path: consecutive chunks per work unit (1 = one chunk)
+  int32_t nseg_off;     // int offset inside plan of the number of segments (varlen)
 };
 
 // Ints ahead of the per-(sequence, head) counters in Args::sync.
 constexpr int kSyncHeader = 64;
+
+// Packed sequences up to which the plan orders the chained kernel's work
+// units by their index inside the sequence (above it: sequence by sequence,
+// one chunk per unit).
+constexpr int kOrderMaxSeqs = 4096;
 
 // Chunk c's place in the token stream.
 struct Chunk {
@@ -173,6 +180,9 @@ bool fused_path_supports(const Args &a);
 hipError_t launch_fused(const Args &a, const void *cb, const void *zeros, hipStream_t s);
 bool chain_path_supports(const Args &a);
 hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream_t s);
+int chain_segment(const Args &a);
+bool f32seq_path_supports(const Args &a);
+hipError_t launch_f32seq(const Args &a, hipStream_t s);
 hipError_t launch_final_of_empty(const Args &a, hipStream_t s);
 
 }  // namespace ssd

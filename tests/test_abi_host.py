@@ -445,3 +445,17 @@ def test_conv_rejects_tensor_on_another_device(name):
     a[name] = torch.zeros(a[name].shape, dtype=a[name].dtype)
     with pytest.raises(ValueError, match=name):
         ssd.conv1d_silu(_meta(2, 32, ch), a["weight"], a["bias"], 64, 16, a["history"])
+
+
+@pytest.mark.parametrize("kw,units", [
+    (dict(batch=8, seqlen=2048, nheads=80), 2),            # 5,120 one-chunk units: segments of 2
+    (dict(batch=4, seqlen=2048, nheads=24), 1),            # 768 units: all fit the chip at once
+    (dict(batch=2, seqlen=16384, nheads=64, dstate=256, ngroups=8), 1),   # N = 256
+    (dict(batch=1, seqlen=137028, nheads=80, num_seqs=64), 1),            # packed sequences
+    (dict(batch=8, seqlen=2048, nheads=80, flags=ssd.SSD_FLAG_UNFUSED), 0),  # no chained kernel
+    (dict(batch=8, seqlen=2048, nheads=80, dtype=ssd.SSD_DTYPE_F32), 0),
+])
+def test_chained_chunks_per_unit(lib, kw, units):
+    base = dict(ngroups=1, dstate=128)
+    base.update(kw)
+    assert ssd.workspace_layout(P(**base)).chain_chunks_per_unit == units

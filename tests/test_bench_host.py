@@ -41,14 +41,29 @@ def test_chain_cost_of_the_2_7b_workload_by_hand():
     assert cost["ssd_chain"]["bytes"] == want == cost["ssd_fused"]["bytes"]
     # ... and reports the state hand-off between chunk workgroups apart
     assert cost["ssd_chain"]["overhead_bytes"] == (chunks - seqs) * H * handoff == 293_601_280
+    # with two chunks per work unit only every second boundary is handed off:
+    # 4 units per sequence, 3 hand-offs
+    two = bench.algorithmic_cost(w, inp, chunks_per_unit=2)
+    assert two["ssd_chain"]["overhead_bytes"] == seqs * 3 * H * handoff == 125_829_120
+    assert two["ssd_chain"]["bytes"] == want
     # masked product 2 tri P, chunk state and C h_in 2 x 2 q N P, state carry 2 P N
     flops = chunks * H * (2 * tri * P + 4 * q * N * P + 2 * P * N)
     assert cost["ssd_chain"]["flops"] == flops
 
 
-def test_traffic_record_follows_the_kernel_sources(monkeypatch):
-    rec = bench.measured_traffic("ssd_chain", "2.7b-bf16")
-    assert isinstance(rec, int) and rec > 0
-    monkeypatch.setattr(bench, "kernel_sources_sha256", lambda files: "0" * 64)
-    assert bench.measured_traffic("ssd_chain", "2.7b-bf16") is None
-    assert bench.measured_traffic("no_such_kernel", "2.7b-bf16") is None
+def test_traffic_record_follows_the_kernel_sources(monkeypatch, tmp_path):
+    """A counter record is reported only while the hash of the kernel sources
+    it names matches the one written in it."""
+    csrc = tmp_path / "mamba_ssd_sequence_fwd_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "k_demo.hip").write_text("// kernel v1\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setitem(bench.TRAFFIC_PROFILES, ("demo", "w"), ("demo.md", ("k_demo.hip",)))
+    digest = bench.kernel_sources_sha256(("k_demo.hip",))
+    (tmp_path / "profiles" / "demo.md").write_text(
+        "# demo\n\n- kernel_sources_sha256: `%s`\n- hbm_bytes_per_launch: `123456`\n" % digest)
+    assert bench.measured_traffic("demo", "w") == 123456
+    (csrc / "k_demo.hip").write_text("// kernel v2\n")
+    assert bench.measured_traffic("demo", "w") is None
+    assert bench.measured_traffic("no_such_kernel", "w") is None
