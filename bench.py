@@ -95,9 +95,13 @@ def algorithmic_cost(w: si.Workload, inp: dict, chunks_per_unit: int = 1) -> dic
 # HBM bytes per launch of the dominant kernel, measured with rocprofv3 FETCH_SIZE
 # and WRITE_SIZE passes and recorded in profiles/ with the hash of the kernel
 # sources they were taken on. Reported only while the sources still match.
+_CHAIN_SRC = ("k_chain.hip", "mfma_common.h", "ssd_internal.h")
 TRAFFIC_PROFILES = {
-    ("ssd_chain", "2.7b-bf16"): ("ssd_chain_2.7b-bf16_hbm_bytes.md",
-                                 ("k_chain.hip", "mfma_common.h", "ssd_internal.h")),
+    ("ssd_chain", "2.7b-bf16"): ("ssd_chain_2.7b-bf16.md", _CHAIN_SRC),
+    ("ssd_chain", "small-bf16"): ("ssd_chain_small-bf16.md", _CHAIN_SRC),
+    ("ssd_chain", "large-state-long"): ("ssd_chain_large-state-long.md", _CHAIN_SRC),
+    ("ssd_chain", "varlen-packed"): ("ssd_chain_varlen-packed.md", _CHAIN_SRC),
+    ("ssd_f32seq", "tiny-fp32"): ("ssd_f32seq_tiny-fp32.md", ("k_f32seq.hip", "ssd_internal.h")),
     ("ssd_step", "decode-2.7b-b256"): ("ssd_step_decode-2.7b-b256.md",
                                        ("k_step.hip", "step.h", "ssd_internal.h")),
     ("ssd_conv", "conv-front-2.7b"): ("ssd_conv_front-2.7b.md",
