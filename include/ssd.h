@@ -161,6 +161,31 @@ ssd_status ssd_forward(const ssd_problem *prob, const void *x, const void *dt,
                        const int32_t *cu_seqlens, void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* ssd_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same operation, arguments, layouts and
+ * kernels as ssd_forward; the workspace is instead a fixed scratch area of
+ * 64 MiB that the library keeps in device memory on every GPU it runs on
+ * (held until the process ends; its address is looked up on the first call
+ * on a device, with that device current). The current device must be the
+ * stream's device. Nothing is allocated, freed or synchronised.
+ * Returns SSD_ERR_WORKSPACE, before anything is enqueued, for problems whose
+ * workspace (ssd_workspace_size) exceeds 64 MiB; use ssd_forward for those.
+ * On the default bf16 path the state hand-off takes 64 KiB per (sequence,
+ * head) at P = 64, N = 128 and the C B^T and B^T tiles about 136 KiB per
+ * (chunk, group) at chunk 256, so the 2.7B-shaped batch (8 sequences of
+ * 2048 tokens, 80 heads: about 51 MB) fits and the 64-sequence packed batch
+ * does not.
+ * All calls on one GPU share its scratch area, and each pass clears what it
+ * needs cleared itself: calls that may overlap on one GPU (on different
+ * streams, or from several host threads) race and give wrong results; order
+ * them on one stream. */
+ssd_status ssd_forward_noalloc(const ssd_problem *prob, const void *x, const void *dt,
+                               const float *A, const void *B, const void *C,
+                               const float *D, const float *initial_state,
+                               const int32_t *cu_seqlens, void *y, float *final_state,
+                               void *stream);
+
 /* ssd_forward with the step activation fused in: dt_raw holds the step's
  * pre-activation and every kernel uses
  *   dt[t, h] = softplus(dt_raw[t, h] + dt_bias[h]),  softplus(v) = log(1 + e^v)

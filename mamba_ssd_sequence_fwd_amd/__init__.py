@@ -13,7 +13,8 @@ with ``python -m mamba_ssd_sequence_fwd_amd.build``.
 """
 from ._lib import (  # noqa: F401
     EXPORTED, LIB_PATH, BackwardPlan, ConvProblem, Plan, Problem, ScanProblem, SSDError,
-    StageTimes, WorkspaceLayout, backward, conv1d_silu, forward, load, selective_scan,
+    StageTimes, WorkspaceLayout, backward, conv1d_silu, forward, forward_noalloc, load,
+    selective_scan,
     make_problem, step, validate, validate_cu_seqlens, workspace_layout, workspace_size,
     SSD_DTYPE_BF16, SSD_DTYPE_F32, SSD_FLAG_GENERIC_KERNELS, SSD_FLAG_UNFUSED, SSD_FLAG_PER_SEQUENCE,
     SSD_OK,

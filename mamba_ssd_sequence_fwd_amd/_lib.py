@@ -78,7 +78,8 @@ class StageTimes(ctypes.Structure):
 
 
 EXPORTED = ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-            "ssd_forward", "ssd_forward_dt_softplus", "ssd_forward_timed", "ssd_step",
+            "ssd_forward", "ssd_forward_noalloc", "ssd_forward_dt_softplus",
+            "ssd_forward_timed", "ssd_step",
             "ssd_selective_scan", "ssd_conv1d_silu",
             "ssd_backward_workspace_size", "ssd_backward", "ssd_backward_timed",
             "ssd_get_workspace_layout",
@@ -106,6 +107,7 @@ def load(path: str = LIB_PATH):
         lib.ssd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         lib.ssd_get_workspace_layout.argtypes = [P, ctypes.POINTER(WorkspaceLayout)]
         lib.ssd_forward.argtypes = [P] + [vp] * 11 + [ctypes.c_size_t, vp]
+        lib.ssd_forward_noalloc.argtypes = [P] + [vp] * 11
         lib.ssd_forward_timed.argtypes = ([P] + [vp] * 11 + [ctypes.c_size_t, vp, ctypes.c_int32,
                                           ctypes.POINTER(StageTimes)])
         lib.ssd_step.argtypes = [P] + [vp] * 9
@@ -117,7 +119,8 @@ def load(path: str = LIB_PATH):
         lib.ssd_backward_timed.argtypes = ([P] + [vp] * 18 + [ctypes.c_size_t, vp,
                                            ctypes.c_int32, ctypes.POINTER(StageTimes)])
         for f in ("ssd_validate", "ssd_validate_cu_seqlens", "ssd_workspace_size",
-                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_timed", "ssd_step",
+                  "ssd_get_workspace_layout", "ssd_forward", "ssd_forward_noalloc",
+                  "ssd_forward_timed", "ssd_step",
                   "ssd_selective_scan", "ssd_forward_dt_softplus"):
             getattr(lib, f).restype = ctypes.c_int
         lib.ssd_status_string.argtypes = [ctypes.c_int]
@@ -338,6 +341,52 @@ def forward(x, dt, A, B, C, D=None, initial_state=None, chunk_size=256, cu_seqle
     if check:
         plan.check()
     return y, hT
+
+
+def forward_noalloc(x, dt, A, B, C, D, initial_state, y, final_state, chunk_size=256,
+                    cu_seqlens=None, *, stream=None):
+    """ssd_forward_noalloc: the forward pass into caller-provided ``y`` and
+    ``final_state`` (or None) with the library's fixed device scratch area as
+    the workspace; nothing is allocated. Tensors as for :class:`Plan`, all on
+    one GPU; ``cu_seqlens`` int32 on that GPU (no host copy, no check of its
+    values here). Calls that may overlap on one GPU race on the scratch area.
+    """
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seqlen, nheads, headdim)")
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    _same_device(dev, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, y=y,
+                 final_state=final_state, cu_seqlens=cu_seqlens)
+    _on_gpu(dev)
+    if x.dtype not in _DTYPES:
+        raise ValueError("x must be bfloat16 or float32")
+    num_seqs = 0 if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or batch != 1):
+        raise ValueError("cu_seqlens must be int32 with batch == 1")
+    nstate = num_seqs if num_seqs else batch
+    for name, t, shape, dtype in (
+            ("dt", dt, (batch, L, H), x.dtype), ("B", B, (batch, L, G, N), x.dtype),
+            ("C", C, (batch, L, G, N), x.dtype), ("A", A, (H,), torch.float32),
+            ("D", D, (H,), torch.float32), ("y", y, (batch, L, H, P), x.dtype),
+            ("initial_state", initial_state, (nstate, H, P, N), torch.float32),
+            ("final_state", final_state, (nstate, H, P, N), torch.float32)):
+        if t is None and name in ("dt", "B", "C", "A", "y"):
+            raise ValueError("%s is required" % name)
+        if t is not None and (tuple(t.shape) != shape or t.dtype != dtype
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous %s %s tensor" % (name, shape, dtype))
+    for name, t in (("x", x), ("cu_seqlens", cu_seqlens)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    prob = make_problem(batch, L, H, P, N, G, chunk_size, num_seqs, _DTYPES[x.dtype], 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    _check(load().ssd_forward_noalloc(
+        ctypes.byref(prob), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(initial_state), _ptr(cu_seqlens), _ptr(y), _ptr(final_state),
+        ctypes.c_void_p(stream.cuda_stream)), "ssd_forward_noalloc")
+    return y, final_state
 
 
 def step(x, dt, A, B, C, D=None, state=None, *, y=None, stream=None):

@@ -23,6 +23,8 @@
 
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -454,6 +456,43 @@ ssd_status prepare_bwd(const ssd_problem *p, const void *x, const void *dt, cons
   return SSD_OK;
 }
 
+// ---- allocation-free entry point ------------------------------------------------
+// The workspace of ssd_forward_noalloc: a file-scope device array (one copy on
+// every GPU the library runs on, held until the process ends). In host code
+// `scratch` names a host-side stand-in, not device memory, so kernels are
+// given the device address looked up once per device below.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's `scratch`, looked up on the first call on
+// the device (with that device current) and kept; nullptr on failure.
+void *scratch_for_current_device(int *dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(SSD_ERR_HIP, "hipGetDevice failed or device index %d above %d", dev, kMaxDevices - 1);
+    return nullptr;
+  }
+  *dev_out = dev;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void *q = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || q == nullptr) {
+    fail(SSD_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+         hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -573,6 +612,30 @@ ssd_status ssd_forward(const ssd_problem *p, const void *x, const void *dt,
                                 final_state, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return enqueue(a, L, p->dtype == SSD_DTYPE_BF16, s, nullptr);
+}
+
+ssd_status ssd_forward_noalloc(const ssd_problem *p, const void *x, const void *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               const float *initial_state, const int32_t *cu_seqlens, void *y,
+                               float *final_state, void *stream) {
+  g_detail.clear();
+  ssd_status st = ssd_validate(p);
+  if (st != SSD_OK) return st;
+  const Layout L = make_layout(*p);
+  if (L.total > kScratchBytes)
+    return fail(SSD_ERR_WORKSPACE,
+                "the problem needs %zu bytes of workspace; the allocation-free entry point has "
+                "a fixed %zu-byte scratch area (call ssd_forward with a workspace instead)",
+                L.total, kScratchBytes);
+  int dev = -1;
+  void *ws = scratch_for_current_device(&dev);
+  if (!ws) return SSD_ERR_HIP;
+  st = check_args(p, x, dt, A, B, C, cu_seqlens, y, initial_state, final_state, ws,
+                  kScratchBytes);
+  if (st != SSD_OK) return st;
+  const ssd::Args a = make_args(p, L, x, dt, A, B, C, D, initial_state, cu_seqlens, y,
+                                final_state, ws);
+  return enqueue(a, L, p->dtype == SSD_DTYPE_BF16, static_cast<hipStream_t>(stream), nullptr);
 }
 
 ssd_status ssd_forward_dt_softplus(const ssd_problem *p, const void *x, const void *dt_raw,

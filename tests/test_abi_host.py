@@ -459,3 +459,13 @@ def test_chained_chunks_per_unit(lib, kw, units):
     base = dict(ngroups=1, dstate=128)
     base.update(kw)
     assert ssd.workspace_layout(P(**base)).chain_chunks_per_unit == units
+
+
+def test_noalloc_refuses_a_problem_above_its_scratch(lib):
+    """The allocation-free entry point checks the workspace the problem needs
+    against its fixed scratch area before touching the device."""
+    prob = ssd.make_problem(1, 137028, 80, 64, 128, 1, 256, 64, ssd.SSD_DTYPE_BF16, 0)
+    assert ssd.workspace_size(prob) > 64 << 20
+    st = lib.ssd_forward_noalloc(ctypes.byref(prob), *([None] * 11))
+    assert st == ssd.SSD_ERR_WORKSPACE
+    assert b"scratch" in lib.ssd_last_error_detail()
