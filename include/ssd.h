@@ -329,7 +329,7 @@ ssd_status ssd_step(const ssd_problem *prob, const void *x, const void *dt,
  * nothing is enqueued on error. One kernel, no allocation, no workspace. */
 typedef struct ssd_scan_problem {
   int32_t batch, seqlen, dim, dstate;
-  ssd_dtype dtype;
+  int32_t dtype;      /* an ssd_dtype value (int32_t so that any value can be checked) */
   uint32_t flags;
 } ssd_scan_problem;
 ssd_status ssd_selective_scan(const ssd_scan_problem *prob, const void *x, const void *delta,
@@ -438,7 +438,7 @@ ssd_status ssd_backward_timed(const ssd_problem *prob, const void *x, const void
 typedef struct ssd_conv_problem {
   int32_t batch, seqlen, num_seqs;
   int32_t x_dim, bc_dim, width, in_stride;
-  ssd_dtype dtype;
+  int32_t dtype;      /* an ssd_dtype value (int32_t so that any value can be checked) */
   uint32_t flags;
 } ssd_conv_problem;
 ssd_status ssd_conv1d_silu(const ssd_conv_problem *prob, const void *xbc, const float *weight,

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   const int S = a.nseq, Q = a.Q;
   int *first = a.plan + 2;  // first chunk of each sequence, then the total
   int4 *rec = reinterpret_cast<int4 *>(a.plan + a.rec_off);
-  if (tid == 0) s_bad = (a.cu[0] != 0 || a.cu[S] != a.L) ? 1 : 0;
+  if (tid == 0) s_bad = stream_ends_ok(a.cu[0], a.cu[S], a.L) ? 0 : 1;
   __syncthreads();
 
   int carry = 0;  // chunks of all earlier tiles
@@ -31,9 +31,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
     const int s = base + tid;
     int cnt = 0;
     if (s < S) {
-      const int lo = a.cu[s], hi = a.cu[s + 1];
-      if (hi < lo || lo < 0 || hi > a.L) s_bad = 1;  // benign race: all write 1
-      else cnt = (hi - lo + Q - 1) / Q;
+      const int n = seq_chunk_count(a.cu[s], a.cu[s + 1], a.L, Q);
+      if (n < 0) s_bad = 1;  // benign race: all write 1
+      else cnt = n;
     }
     // Block-wide exclusive scan of cnt: wave scan, then scan of wave totals.
     const int incl = wave_inclusive_sum(cnt);

@@ -556,14 +556,24 @@ ssd_status ssd_validate_cu_seqlens(const ssd_problem *p, const int32_t *cu) {
   if (st != SSD_OK) return st;
   if (p->num_seqs <= 0) return fail(SSD_ERR_INVALID_ARG, "problem is not varlen (num_seqs 0)");
   if (!cu) return fail(SSD_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  // the same checks the device plan kernel applies (ssd::seq_chunk_count,
+  // ssd::stream_ends_ok), with a message naming the first offending entry
   if (cu[0] != 0) return fail(SSD_ERR_INVALID_ARG, "cu_seqlens[0] = %d, must be 0", cu[0]);
-  for (int s = 0; s < p->num_seqs; ++s)
-    if (cu[s + 1] < cu[s])
-      return fail(SSD_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s],
-                  cu[s + 1]);
-  if (cu[p->num_seqs] != p->seqlen)
+  int64_t chunks = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int n = ssd::seq_chunk_count(cu[s], cu[s + 1], p->seqlen, p->chunk_size);
+    if (n < 0)
+      return fail(SSD_ERR_INVALID_ARG,
+                  "cu_seqlens[%d..%d] = (%d, %d) is not a sequence of the %d tokens", s, s + 1,
+                  cu[s], cu[s + 1], p->seqlen);
+    chunks += n;
+  }
+  if (!ssd::stream_ends_ok(cu[0], cu[p->num_seqs], p->seqlen))
     return fail(SSD_ERR_INVALID_ARG, "cu_seqlens[%d] = %d, must equal seqlen %d",
                 p->num_seqs, cu[p->num_seqs], p->seqlen);
+  if (chunks > make_layout(*p).nc_max)  // cannot happen once the checks above pass
+    return fail(SSD_ERR_INVALID_ARG, "cu_seqlens give %lld chunks, more than the layout's %lld",
+                (long long)chunks, (long long)make_layout(*p).nc_max);
   return SSD_OK;
 }
 

@@ -54,6 +54,18 @@ constexpr int kSyncHeader = 64;
 // one chunk per unit).
 constexpr int kOrderMaxSeqs = 4096;
 
+// Checks of packed-sequence offsets, shared by the device plan kernel (which
+// must never index out of bounds whatever the device cu_seqlens hold) and
+// the host validation of cu_seqlens:
+// chunks of sequence [lo, hi) of a stream of L tokens, or -1 if malformed,
+__host__ __device__ inline int seq_chunk_count(int lo, int hi, int L, int Q) {
+  return (hi < lo || lo < 0 || hi > L) ? -1 : (hi - lo + Q - 1) / Q;
+}
+// and whether the offsets start at 0 and end at the stream's length.
+__host__ __device__ inline bool stream_ends_ok(int first, int last, int L) {
+  return first == 0 && last == L;
+}
+
 // Chunk c's place in the token stream.
 struct Chunk {
   int32_t seq;    // sequence (batch row) it belongs to

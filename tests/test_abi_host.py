@@ -80,9 +80,19 @@ def test_error_detail_names_the_problem(lib):
 
 @pytest.mark.parametrize("cu,status", [
     ([0, 10, 10, 25, 40], ssd.SSD_OK),            # an empty sequence is allowed
+    ([0, 0, 0, 0, 40], ssd.SSD_OK),
     ([1, 10, 20, 30, 40], ssd.SSD_ERR_INVALID_ARG),
     ([0, 10, 5, 30, 40], ssd.SSD_ERR_INVALID_ARG),
     ([0, 10, 20, 30, 39], ssd.SSD_ERR_INVALID_ARG),
+    # malformed in the ways the device plan kernel guards against: negative
+    # offsets, offsets past the stream, a sequence running backwards past 0,
+    # int32 extremes (none may make either side index out of bounds)
+    ([0, -5, 20, 30, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([0, 10, 50, 30, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([0, 41, 41, 41, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([0, 2 ** 31 - 1, 20, 30, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([0, -2 ** 31, 20, 30, 40], ssd.SSD_ERR_INVALID_ARG),
+    ([-2 ** 31, 10, 20, 30, 40], ssd.SSD_ERR_INVALID_ARG),
 ])
 def test_validate_cu_seqlens(lib, cu, status):
     prob = P(batch=1, seqlen=40, num_seqs=4)
