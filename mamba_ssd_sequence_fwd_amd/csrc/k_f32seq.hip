@@ -181,9 +181,22 @@ __global__ __launch_bounds__(kF32Threads) void k_ssd_f32seq(Args a) {
 #pragma unroll
       for (int kk = 0; kk < N / 4; ++kk)
         st = mfma4(sH[(4 * kk + lq) * HS + 16 * pt + lr], sC[l * BS + 4 * kk + lq], st);
-      // intra-chunk part: sum_{s <= l} x[s][p] M[l][s]
-      for (int kk = 0; kk < 4 * (lt + 1); ++kk)
-        in = mfma4(sX[(4 * kk + lq) * XS + 16 * pt + lr], sM[l * MS + 4 * kk + lq], in);
+      // intra-chunk part: sum_{s <= l} x[s][p] M[l][s], one 16-token s tile
+      // at a time: its eight operand reads issued together, then four
+      // independent accumulations (no chain of dependent MFMAs)
+      f32x4v in4[4] = {in, in, in, in};
+      for (int stile = 0; stile <= lt; ++stile) {
+        float xa[4], ma[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int sr = 16 * stile + 4 * q + lq;
+          xa[q] = sX[sr * XS + 16 * pt + lr];
+          ma[q] = sM[l * MS + sr];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) in4[q] = mfma4(xa[q], ma[q], in4[q]);
+      }
+      in = (in4[0] + in4[1]) + (in4[2] + in4[3]);
       const float el = exp2_fast(sCs[l]);
       float4 o;
       float ov[4];
@@ -201,13 +214,17 @@ __global__ __launch_bounds__(kF32Threads) void k_ssd_f32seq(Args a) {
       const int t = wave + 4 * j;
       if (t < NST) {
         const int nt = t / (P / 16), pt = t - nt * (P / 16);
-        f32x4v acc = dec * hs[j];
-#pragma unroll 4
+        // four independent accumulations over the chunk's 64 tokens, the
+        // decayed state entering the first
+        f32x4v acc[4] = {dec * hs[j], f32x4v{0.f, 0.f, 0.f, 0.f}, f32x4v{0.f, 0.f, 0.f, 0.f},
+                         f32x4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
         for (int kk = 0; kk < Q / 4; ++kk) {
           const int sr = 4 * kk + lq;
-          acc = mfma4(sW[sr] * sB[sr * BS + 16 * nt + lr], sX[sr * XS + 16 * pt + lr], acc);
+          acc[kk % 4] = mfma4(sW[sr] * sB[sr * BS + 16 * nt + lr], sX[sr * XS + 16 * pt + lr],
+                              acc[kk % 4]);
         }
-        hs[j] = acc;
+        hs[j] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
     }
   }
