@@ -11,6 +11,8 @@ import numpy as np
 import pytest
 import torch
 
+import mamba_ssd_sequence_fwd_amd as ssd
+
 import oracle
 import ssd_inputs as si
 from gpu_helpers import (PATHS, compare_every_pair, flat_inputs, plan_for, rel_err, run_gpu,
@@ -266,3 +268,31 @@ def test_full_workload_every_pair(name):
     for path, r in res.items():
         assert r["y"] <= tol and r["final"] <= tol, (path, r)
         assert r["worst_y"] <= tol and r["worst_final"] <= tol, (path, r)
+
+
+@pytest.mark.parametrize("path", ["default", "unfused", "fp32"])
+@pytest.mark.parametrize("bad", [[1, 300, 600, 900, 1133], [0, 300, 200, 900, 1133],
+                                 [0, 300, 600, 1500, 1133], [0, 300, 2 ** 31 - 1, 900, 1133],
+                                 [0, -300, 600, 900, 1133]],
+                         ids=["first-not-0", "decreasing", "past-the-end", "int-max", "negative"])
+def test_malformed_device_cu_seqlens_are_flagged_not_followed(bad, path):
+    """Offsets that only the device sees (the host check skipped) and that are
+    malformed: the plan kernel flags them and leaves zero chunks, so no
+    kernel reads or writes a token through them; the pass completes and the
+    flag is readable in the workspace (the outputs are unspecified)."""
+    w = si.scaled(C[4], nheads=4, num_seqs=4, seq_lens=(300, 300, 300, 233), h0_std=0.1,
+                  seed=2110, dtype="fp32" if path == "fp32" else "bf16",
+                  chunk=64 if path == "fp32" else 256, headdim=32 if path == "fp32" else 64,
+                  dstate=32 if path == "fp32" else 128)
+    inp = si.make_inputs(w)
+    d = {k: (None if inp[k] is None else inp[k].cuda()) for k in ("x", "dt", "A", "B", "C", "D", "h0")}
+    cu = torch.tensor(bad, dtype=torch.int32, device="cuda")
+    plan = ssd.Plan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk_size=w.chunk,
+                    cu_seqlens=cu, check_cu_seqlens=False, unfused=path == "unfused")
+    print("[gpu] malformed device cu_seqlens %s path=%s %r" % (bad, path, plan.prob), flush=True)
+    plan.run()
+    torch.cuda.synchronize()
+    assert plan.chain_error() == 0
+    lay = plan.layout()
+    header = plan.workspace[lay.chunk_table:lay.chunk_table + 8].view(torch.int32).cpu()
+    assert int(header[0]) == 0 and int(header[1]) == 1, header.tolist()
