@@ -204,36 +204,62 @@ __device__ __forceinline__ void state_tile(int i, f32x4 (&Y)[2][4], const bf16 *
   }
 }
 
+__device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
+  // lanes 2k and 2k + 1 exchange v (DPP quad_perm [1, 0, 3, 2])
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+}
+
+// y rows of the 32-row tile i, both halves. A lane holds, for its row l, four
+// p tiles of packed values; lanes 16 apart (same row l) exchange one p tile's
+// worth so that each lane holds 8 consecutive p, a 16-byte piece (v_permlane16
+// _swap swaps the odd 16-lane rows of its first operand with the even rows of
+// its second, so after swapping (p tile 2m, p tile 2m+1) every lane holds its
+// output in order). The four lanes of a row then hold its two 64-byte halves
+// m = 0, 1; adjacent lanes (rows 2k, 2k + 1) swap one half more, so that in
+// each of two stores lane 2k + m writes half m of row 2k, then of row 2k + 1:
+// every store instruction writes eight whole 128-byte rows.
 __device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int len, bf16 *y,
                                            size_t ystride, int lane) {
-  // Lanes 16 apart (same row l) exchange one p tile's worth of packed values
-  // so that each lane holds 8 consecutive p: 16-byte stores, 64 contiguous
-  // bytes per row and instruction. v_permlane16_swap swaps the odd 16-lane
-  // rows of its first operand with the even rows of its second, so after
-  // swapping (p tile 2m, p tile 2m+1) every lane holds its output in order.
   const int lr = lane & 15, lg = lane >> 4;
+  const int odd = lr & 1;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int l = 32 * i + 16 * u + lr;
     uint32_t pk[4][2];
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       pk[pt][0] = pack2(Y[u][pt][0], Y[u][pt][1]);
       pk[pt][1] = pack2(Y[u][pt][2], Y[u][pt][3]);
     }
-    bf16 *yr = y + (size_t)l * ystride + 8 * (lg >> 1) + 16 * (lg & 1);
+    uint32_t o[2][4];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const auto sx = __builtin_amdgcn_permlane16_swap(pk[2 * m][0], pk[2 * m + 1][0], false, false);
       const auto sy = __builtin_amdgcn_permlane16_swap(pk[2 * m][1], pk[2 * m + 1][1], false, false);
-      const uint4 o = make_uint4(sx[0], sy[0], sx[1], sy[1]);
-      // y is written once and read by nothing in this pass: nontemporal
-      // stores (measured 5-8% faster on the 2.7B-shaped workload, 2%
-      // slower on the long varlen one)
-      if (l < len) {
-        const u32x4_t ov = {o.x, o.y, o.z, o.w};
-        __builtin_nontemporal_store(ov, reinterpret_cast<u32x4_t *>(yr + 32 * m));
-      }
+      o[m][0] = sx[0];
+      o[m][1] = sy[0];
+      o[m][2] = sx[1];
+      o[m][3] = sy[1];
+    }
+    uint32_t fa[4], fb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t recv = swap_adjacent(odd ? o[0][e] : o[1][e]);
+      fa[e] = odd ? recv : o[0][e];
+      fb[e] = odd ? o[1][e] : recv;
+    }
+    // y is written once and read by nothing in this pass: nontemporal stores
+    // of whole rows (order-balanced A/B against 64-byte half rows: the
+    // 2.7B-shaped workload 176 -> 164 us per pass, the long packed one
+    // 1691 -> 1586 us)
+    const int ra = 32 * i + 16 * u + (lr & ~1);
+    bf16 *ya = y + (size_t)ra * ystride + 8 * (lg >> 1) + 16 * (lg & 1) + 32 * odd;
+    if (ra < len) {
+      const u32x4_t va = {fa[0], fa[1], fa[2], fa[3]};
+      __builtin_nontemporal_store(va, reinterpret_cast<u32x4_t *>(ya));
+    }
+    if (ra + 1 < len) {
+      const u32x4_t vb = {fb[0], fb[1], fb[2], fb[3]};
+      __builtin_nontemporal_store(vb, reinterpret_cast<u32x4_t *>(ya + ystride));
     }
   }
 }
@@ -372,7 +398,6 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     chunks_of_seq(a, k0.seq, q0, q1);
     nk = min(a.seg, q1 - c0);
   }
-  const int g = h / a.heads_per_group;
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N, PN = (size_t)kP * N;
   f32x4 hcarry[NTW][4];  // kSeg: the state leaving the previous chunk of the segment
 
@@ -381,6 +406,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   // live (in registers) across the whole walk.
   auto chunk_body = [&](const int ci, const int tid) -> bool {
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int g = h / a.heads_per_group;
   const int c = c0 + ci;
   Chunk k;
   if (!chunk_of(a, c, k)) return false;
