@@ -29,9 +29,9 @@
 //      (the chunk_scan step); y.
 //
 // For dense problems with more units than the chip holds, a work unit is a
-// segment of two consecutive chunks of one (sequence, head), walked by one
-// workgroup with the state passed between them in registers (kSeg below), so
-// only every second chunk boundary goes through the ring.
+// segment of up to four consecutive chunks of one (sequence, head), walked by
+// one workgroup with the state passed between them in registers (kSeg below),
+// so only every fourth chunk boundary goes through the ring.
 //
 // Tickets from an atomic counter order the work units by chunk index inside
 // the sequence, then sequence, then head, so the predecessor of a unit took
@@ -643,12 +643,14 @@ bool chain_path_supports(const Args &a) {
 constexpr int64_t kDeepMaxUnits = 3 * 256;
 
 // Chunks per work unit for problems with more units than the chip holds at
-// once. Order-balanced A/B, same box: the 2.7B-shaped workload 186.5 -> 174.2
-// us per pass with segments of 2 (4: 173.6; 8: 199.3), the long packed one
-// 1687 -> 1816 us (4: 1727). The packed workload is the more sensitive to the
-// third workgroup per CU that segments give up, so packed input keeps
-// one-chunk units.
-constexpr int kChainSeg = 2;
+// once. Order-balanced A/B on one box, with whole-row y stores, the 2.7B-shaped
+// workload: units of 1, 2, 3 and 4 chunks within 3% of each other (163-170 us
+// per pass over two rounds), so the longest is taken: it moves the fewest
+// hand-off bytes (42 MB per launch against 294 MB for one-chunk units). The
+// long packed workload lost with segments (1586 -> 1631 us with units of 2),
+// being the more sensitive to the third workgroup per CU that segments give
+// up, so packed input keeps one-chunk units.
+constexpr int kChainSeg = 4;
 
 int chain_segment(const Args &a) {
   if (a.N == 256 || a.varlen) return 1;
