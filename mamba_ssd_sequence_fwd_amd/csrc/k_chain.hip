@@ -349,6 +349,18 @@ __device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, c
 // writes the ring and only its first reads it: a segment of k chunks moves
 // 1/k of the hand-off bytes of k one-chunk units. The carried state costs 32
 // registers (N = 128), so segments run two workgroups per CU.
+//
+// kSeg with a.nrange > 0 (dense input with at least as many (sequence, head)
+// pairs as the chip holds workgroups): instead of equal segments, workgroup
+// k takes the k-th of a.nrange balanced ranges of the chunk order (sequence,
+// head, chunk index), so that every workgroup walks the same number of
+// chunks and none is left for a partial last wave. A range holds at least
+// one pair's worth of chunks, so it is a run of whole pairs with at most a
+// partial pair at each end: one that continues the previous range's last
+// pair and one that the next range continues. The workgroup walks its last
+// part first (it starts at a pair's first chunk and waits on nothing), then
+// the whole pairs, then the first part, whose predecessor the previous
+// workgroup (a smaller ticket) walked first.
 template <int N, int Q, bool kDeep, bool kSeg>
 __global__ __launch_bounds__(64 * kChainWaves)
 __attribute__((amdgpu_waves_per_eu(N == 256 || kDeep || kSeg ? 2 : 3,
@@ -377,8 +389,13 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   if (tid == 0) sTicket = atomicAdd(ticket, 1);
   __syncthreads();
   const int tk = sTicket;
-  int c0, h, nk = 1;
-  if (!a.varlen) {
+  int c0 = 0, h = 0, nk = 1;
+  int64_t rlo = 0, rhi = 0;  // range mode: [rlo, rhi) of the (sequence, head, chunk) order
+  if (kSeg && a.nrange > 0) {
+    const int64_t units = (int64_t)a.nseq * a.H * a.nc_per;
+    rlo = (int64_t)tk * units / a.nrange;
+    rhi = (int64_t)(tk + 1) * units / a.nrange;
+  } else if (!a.varlen) {
     const int per = a.nseq * a.H;
     const int j = tk / per, r = tk - j * per, s = r / a.H;
     h = r - s * a.H;
@@ -399,41 +416,63 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     nk = min(a.seg, q1 - c0);
   }
   const size_t ldx = (size_t)a.H * kP, ldb = (size_t)a.G * N, PN = (size_t)kP * N;
+  // per-head constants, read once per run of chunks of one head
+  float ah, dsk, dtb;
+  auto set_head = [&]() {
+    ah = a.A[h] * kLog2eChain;
+    dsk = a.D ? a.D[h] : 0.f;
+    dtb = a.dt_softplus && a.dt_bias ? a.dt_bias[h] : 0.f;
+  };
   f32x4 hcarry[NTW][4];  // kSeg: the state leaving the previous chunk of the segment
+  // kSeg, dense input: dt and x of the segment's next chunk, loaded by the
+  // chunk before it ahead of its last y stores (a load issued after those
+  // stores could only be waited for together with them)
+  bf16 dt_next;
+  bf16x8 x_next[NKS];
+  // x rows of one chunk into registers, one instruction per 32-token step
+  // (instruction k of wave w: rows 32k + 8w + lane/8, 16 bytes each; rows
+  // past len repeat the last row)
+  auto load_x = [&](const bf16 *xc, int len, int lane, bf16x8 (&dst)[NKS]) {
+    const char *xb = reinterpret_cast<const char *>(xc);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int r = 32 * ks + 8 * wave + (lane >> 3);
+      dst[ks] = *reinterpret_cast<const bf16x8 *>(
+          xb + (uint32_t)min(r, len - 1) * (uint32_t)(ldx * 2) + 16u * (uint32_t)(lane & 7));
+    }
+  };
 
   // One chunk of the work unit; `tid` is passed in so that a segment's loop
   // recomputes the lane-derived offsets per chunk instead of keeping them
   // live (in registers) across the whole walk.
-  auto chunk_body = [&](const int ci, const int tid) -> bool {
+  // `after` = some chunk of this workgroup came before (whose outputs must
+  // have read LDS before it is refilled).
+  auto chunk_body = [&](const int ci, const int tid, const bool after) -> bool {
   const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const int g = h / a.heads_per_group;
   const int c = c0 + ci;
   Chunk k;
   if (!chunk_of(a, c, k)) return false;
-  if (kSeg && ci > 0) __syncthreads();  // the previous chunk's outputs have read LDS
+  if (kSeg && after) __syncthreads();
   const bool head = !kSeg || ci == 0;   // first chunk of the work unit
   const bool tail = !kSeg || ci == nk - 1;  // last chunk of the work unit
   const bf16 *xc = static_cast<const bf16 *>(a.x) + (size_t)k.start * ldx + (size_t)h * kP;
   const bf16 *cc = static_cast<const bf16 *>(a.C) + (size_t)k.start * ldb + (size_t)g * N;
   // ---- 1. loads, decay tables ------------------------------------------------
-  // Loads in the order they are needed (vector memory loads complete in
-  // issue order): dt, the predecessor poll, the first B^T tiles, then x into
-  // registers, one instruction per 32-token step (instruction k of wave w:
-  // rows 32k + 8w + lane/8, 16 bytes each). x reaches LDS step by step, so
-  // S_c starts once the first half has arrived.
-  float dtv;
-  {
-    const int t = min(tid, k.len - 1);
-    const float d = dt_of(a, (float)static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h], h);
-    dtv = tid < k.len ? d : 0.f;  // zero past the chunk end (and for tid >= Q)
-  }
+  // Every load is issued before any result is used, in the order they are
+  // needed (vector memory loads complete in issue order): dt, the predecessor
+  // poll, the first B^T tiles, then x into registers, one instruction per
+  // 32-token step (instruction k of wave w: rows 32k + 8w + lane/8, 16 bytes
+  // each). x reaches LDS step by step, so S_c starts once the first half has
+  // arrived.
+  const bool prefetched = kSeg && !a.varlen && ci > 0;
+  const bf16 dtraw = prefetched ? dt_next
+                                : static_cast<const bf16 *>(a.dt)[(size_t)(k.start + min(tid, k.len - 1)) * a.H + h];
   const int pair = k.seq * a.H + h;
   const bool first = k.idx == 0;
   int early = 0;  // published count of the predecessor, read early
   if (head && !first && tid == 0)
     early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float ah = a.A[h] * kLog2eChain;
-  const float dsk = a.D ? a.D[h] : 0.f;
   const int nt0 = wave * NTW;
   // This wave's B^T operand tiles (n tiles nt0..), streamed KPF 32-token
   // steps ahead of their use; the first KPF steps now.
@@ -446,15 +485,15 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     for (int ks = 0; ks < KPF; ++ks) bts[j][ks] = ldg8(btc + (size_t)(j * NKS + ks) * 512);
   const int xrl = lane >> 3, xcol = lane & 7;
   bf16x8 xr[NKS];
-  {
-    const char *xb = reinterpret_cast<const char *>(xc);
+  if (prefetched) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int r = 32 * ks + 8 * wave + xrl;
-      xr[ks] = *reinterpret_cast<const bf16x8 *>(
-          xb + (uint32_t)min(r, k.len - 1) * (uint32_t)(ldx * 2) + 16u * (uint32_t)xcol);
-    }
+    for (int ks = 0; ks < NKS; ++ks) xr[ks] = x_next[ks];
+  } else {
+    load_x(xc, k.len, lane, xr);
   }
+  float dtv = (float)dtraw;
+  if (a.dt_softplus) dtv = softplus_f32(dtv + dtb);
+  dtv = tid < k.len ? dtv : 0.f;  // zero past the chunk end (and for tid >= Q)
   // x rows of step ks into the swizzled LDS tile (rows past len hold copies
   // of the last row: finite values that are multiplied by zero weights).
   auto put_x = [&](int ks) {
@@ -552,9 +591,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     __syncthreads();
     load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
   }
-  int cs0, cs1;
-  chunks_of_seq(a, k.seq, cs0, cs1);
-  const bool last = c + 1 >= cs1;
+  const bool last = k.last;
   const float dec = exp2_fast(cs_last);
   const __amdgpu_buffer_rsrc_t rout = ring_rsrc(a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN, (int)(PN * 4));
 #pragma unroll
@@ -582,6 +619,17 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     __hip_atomic_store(pub + pair, k.idx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- 4. outputs, one 32-row tile at a time ------------------------------------
+  // dt and x of the segment's next chunk (same sequence: a dense segment
+  // never crosses one), issued after the last C B^T tile loads of this chunk
+  // and before its last y stores
+  auto prefetch_next = [&]() {
+    if (kSeg && !a.varlen && ci + 1 < nk) {
+      const int nstart = k.start + Q, nlen = min(Q, a.L - (k.idx + 1) * Q);
+      dt_next = static_cast<const bf16 *>(a.dt)[(size_t)(nstart + min(tid, nlen - 1)) * a.H + h];
+      load_x(static_cast<const bf16 *>(a.x) + (size_t)nstart * ldx + (size_t)h * kP, nlen, lane,
+             x_next);
+    }
+  };
   const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   bf16 *yc = static_cast<bf16 *>(a.y) + (size_t)k.start * ldx + (size_t)h * kP;
   bf16x8 acB[2][N / 32];
@@ -590,26 +638,53 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     state_tile<N>(iA, Y, sH, sCs, acA, k.len, lane);
     intra_tile<Q>(iA, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
     if (NTILE == 2) load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);  // in flight during the stores
+    else prefetch_next();
     store_tile(iA, Y, k.len, yc, ldx, lane);
   }
   if (NTILE == 2) {
     f32x4 Y[2][4];
     state_tile<N>(iB, Y, sH, sCs, acB, k.len, lane);
     intra_tile<Q>(iB, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
+    prefetch_next();
     store_tile(iB, Y, k.len, yc, ldx, lane);
   }
   return true;
   };  // chunk_body
 
   if constexpr (kSeg) {
+    if (a.nrange > 0) {
+      // parts of the range from the last back to the first
+      bool after = false;
 #pragma unroll 1
-    for (int ci = 0; ci < nk; ++ci) {
-      int t = tid;
-      asm volatile("" : "+v"(t));
-      if (!chunk_body(ci, t)) break;
+      for (int64_t e = rhi; e > rlo;) {
+        const int64_t pair = (e - 1) / a.nc_per;
+        const int64_t b = max(rlo, pair * a.nc_per);
+        const int s = (int)(pair / a.H);
+        h = (int)(pair - (int64_t)s * a.H);
+        c0 = s * a.nc_per + (int)(b - pair * a.nc_per);
+        nk = (int)(e - b);
+        set_head();
+#pragma unroll 1
+        for (int ci = 0; ci < nk; ++ci) {
+          int t = tid;
+          asm volatile("" : "+v"(t));
+          chunk_body(ci, t, after);
+          after = true;
+        }
+        e = b;
+      }
+    } else {
+      set_head();
+#pragma unroll 1
+      for (int ci = 0; ci < nk; ++ci) {
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        if (!chunk_body(ci, t, ci > 0)) break;
+      }
     }
   } else {
-    chunk_body(0, tid);
+    set_head();
+    chunk_body(0, tid, false);
   }
 }
 
@@ -661,7 +736,25 @@ int chain_segment(const Args &a) {
   return kChainSeg;
 }
 
+// Workgroups of the segment kernel that one CU holds (its registers).
+constexpr int kSegWorkgroupsPerCu = 2;
+
+// Balanced ranges (one per workgroup, all resident at once) when a dense
+// problem has at least as many (sequence, head) pairs as the chip holds
+// segment workgroups and more than one chunk per sequence; 0 otherwise.
+// Order-balanced A/B on one box, the 2.7B-shaped workload (640 pairs of 8
+// chunks: 512 workgroups of 10 chunks against 1280 segments of 4, whose last
+// 256 ran as a half-full wave): 165.4 -> 158.9 us per pass, outputs
+// bit-identical.
+int chain_ranges(const Args &a, int compute_units) {
+  if (a.varlen || a.N == 256 || a.seg <= 1 || a.nc_per < 2) return 0;
+  const int64_t slots = (int64_t)compute_units * kSegWorkgroupsPerCu;
+  if (slots <= 0 || (int64_t)a.nseq * a.H < slots) return 0;
+  return (int)slots;
+}
+
 int64_t chain_units(const Args &a) {
+  if (a.nrange > 0) return a.nrange;
   const int s = a.seg;
   if (!a.varlen) return (int64_t)a.nseq * ((a.nc_per + s - 1) / s) * a.H;
   // sum over sequences of ceil(chunks / s) <= (chunks + sequences (s - 1)) / s

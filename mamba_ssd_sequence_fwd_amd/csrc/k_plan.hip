@@ -5,7 +5,8 @@
 // "Boundary Resetting"). Each sequence is cut into ceil(len/Q) chunks of its
 // own, so no chunk straddles a boundary and the state passing between chunks
 // never crosses sequences. One workgroup scans the per-sequence chunk counts
-// and writes one (sequence, first token, length, index) record per chunk.
+// and writes one (sequence, first token, length, index) record per chunk, the
+// index flagged on the sequence's last chunk.
 // Malformed cu_seqlens (cu[0] != 0, decreasing, cu[S] != total) set the error
 // word and leave zero chunks, so every later kernel does nothing.
 #include "ssd_internal.h"
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   for (int s = tid; s < S; s += kPlanThreads) {
     const int lo = a.cu[s], len = a.cu[s + 1] - lo, c0 = first[s];
     for (int i = 0, off = 0; off < len; ++i, off += Q)
-      rec[c0 + i] = make_int4(s, lo + off, min(Q, len - off), i);
+      rec[c0 + i] = make_int4(s, lo + off, min(Q, len - off), i | (off + Q >= len ? kLastChunkFlag : 0));
   }
   // Work-unit order for the chained kernel. A unit is a segment of up to
   // a.seg consecutive chunks of one sequence (a.seg = 1: one chunk), and the

@@ -157,6 +157,25 @@ ssd_status check_args(const ssd_problem *p, const void *x, const void *dt, const
   return SSD_OK;
 }
 
+// Compute units of the current device, cached per device; 256 (MI355X) when
+// no device answers, as for a layout query on a machine without a GPU.
+int device_compute_units() {
+  static int cached[64] = {};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  cached[dev] = n;
+  return n;
+}
+
 ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const void *dt,
                     const float *A, const void *B, const void *C, const float *D,
                     const float *initial_state, const int32_t *cu_seqlens, void *y,
@@ -199,6 +218,7 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.order_off = (int32_t)(L.rec_off + 4 * L.nc_max);
   a.nseg_off = varlen ? 3 + p->num_seqs : 0;
   a.seg = L.path == kMfmaChain ? ssd::chain_segment(a) : 1;
+  a.nrange = L.path == kMfmaChain ? ssd::chain_ranges(a, device_compute_units()) : 0;
   return a;
 }
 
@@ -603,8 +623,13 @@ ssd_status ssd_get_workspace_layout(const ssd_problem *p, ssd_workspace_layout *
     a.N = p->dstate;
     a.H = p->nheads;
     a.varlen = p->num_seqs > 0 ? 1 : 0;
+    a.nseq = a.varlen ? p->num_seqs : p->batch;
+    a.nc_per = a.varlen ? 0 : (p->seqlen + p->chunk_size - 1) / p->chunk_size;
     a.nc_max = (int32_t)L.nc_max;
-    out->chain_chunks_per_unit = ssd::chain_segment(a);
+    a.seg = ssd::chain_segment(a);
+    // balanced ranges walk whole sequences of chunks
+    out->chain_chunks_per_unit =
+        ssd::chain_ranges(a, device_compute_units()) > 0 ? a.nc_per : a.seg;
   }
   return SSD_OK;
 }

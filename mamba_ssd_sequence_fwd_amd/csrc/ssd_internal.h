@@ -44,6 +44,8 @@ struct Args {
   int32_t dt_softplus;  // 0: dt is the step; 1: dt is its pre-activation
   int32_t seg;          // chain path: consecutive chunks per work unit (1 = one chunk)
   int32_t nseg_off;     // int offset inside plan of the number of segments (varlen)
+  int32_t nrange;       // chain path, dense input: > 0 when each workgroup takes one of
+                        // nrange balanced ranges of the (sequence, head, chunk) order
 };
 
 // Ints ahead of the per-(sequence, head) counters in Args::sync.
@@ -72,18 +74,24 @@ struct Chunk {
   int32_t start;  // first token (flat index)
   int32_t len;    // tokens in the chunk, 1..Q
   int32_t idx;    // chunk number inside its sequence
+  bool last;      // the last chunk of its sequence
 };
+
+// Flag on the index field of a packed-input chunk record: the chunk is the
+// last of its sequence (so that no reader needs the sequence's offsets).
+constexpr int32_t kLastChunkFlag = 1 << 30;
 
 // Returns false if chunk slot c is unused (past the last chunk).
 __device__ __forceinline__ bool chunk_of(const Args &a, int c, Chunk &k) {
   int seq, start, len, idx;
-  bool ok;
+  bool ok, last;
   if (!a.varlen) {
     ok = c < a.batch * a.nc_per;
     seq = c / max(a.nc_per, 1);
     idx = c - seq * a.nc_per;
     start = seq * a.L + idx * a.Q;
     len = min(a.Q, a.L - idx * a.Q);
+    last = idx == a.nc_per - 1;
   } else {
     ok = c < a.plan[0];
     const int4 r = ok ? reinterpret_cast<const int4 *>(a.plan + a.rec_off)[c]
@@ -91,12 +99,14 @@ __device__ __forceinline__ bool chunk_of(const Args &a, int c, Chunk &k) {
     seq = r.x;
     start = r.y;
     len = r.z;
-    idx = r.w;
+    idx = r.w & ~kLastChunkFlag;
+    last = (r.w & kLastChunkFlag) != 0;
   }
   k.seq = seq;
   k.start = start;
   k.len = len;
   k.idx = idx;
+  k.last = last;
   return ok;
 }
 
@@ -137,10 +147,12 @@ __device__ __forceinline__ float exp2_fast(float x) {
 // when dt holds the step's pre-activation, softplus(dt + dt_bias[h]) (the
 // selection mechanism's step activation). softplus(v) = log(1 + e^v), taken
 // as v itself above 20 (the difference is below fp32 resolution).
+__device__ __forceinline__ float softplus_f32(float v) {
+  return v > 20.f ? v : log1pf(__expf(v));
+}
 __device__ __forceinline__ float dt_of(const Args &a, float raw, int h) {
   if (!a.dt_softplus) return raw;
-  const float v = raw + (a.dt_bias ? a.dt_bias[h] : 0.f);
-  return v > 20.f ? v : log1pf(__expf(v));
+  return softplus_f32(raw + (a.dt_bias ? a.dt_bias[h] : 0.f));
 }
 
 // ---- wavefront (64-lane) primitives ---------------------------------------
@@ -193,6 +205,7 @@ hipError_t launch_fused(const Args &a, const void *cb, const void *zeros, hipStr
 bool chain_path_supports(const Args &a);
 hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream_t s);
 int chain_segment(const Args &a);
+int chain_ranges(const Args &a, int compute_units);
 bool f32seq_path_supports(const Args &a);
 hipError_t launch_f32seq(const Args &a, hipStream_t s);
 hipError_t launch_final_of_empty(const Args &a, hipStream_t s);
