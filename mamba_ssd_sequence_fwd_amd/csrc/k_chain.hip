@@ -583,8 +583,6 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
 
   // ---- 3. h_in; h_out = 2^(cs_last) h_in + S_c to the ring; publish ------------
   const int iA = wave, iB = T - 1 - wave;
-  bf16x8 acA[2][N / 32];
-  load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);  // used after the hand-off
   if (!ready) {
     if (tid == 0 && !wait_published(pub + pair, k.idx))
       __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -593,21 +591,41 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   }
   const bool last = k.last;
   const float dec = exp2_fast(cs_last);
-  const __amdgpu_buffer_rsrc_t rout = ring_rsrc(a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN, (int)(PN * 4));
+  // The C rows of the first output tile: issued now only when no ring store
+  // follows (the wait for the stores would wait for them too), else after
+  // the publish.
+  bf16x8 acA[2][N / 32];
+  if (!tail) load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);
+  if (!tail) {  // the next chunk of the segment starts from h_out
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hcarry[j][pt] = dec * hin[j][pt] + hs[j][pt];
+  } else if (!last) {
+    const __amdgpu_buffer_rsrc_t rout =
+        ring_rsrc(a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN, (int)(PN * 4));
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+        ring_store4(rout, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16),
+                    dec * hin[j][pt] + hs[j][pt]);
+  } else if (a.hT) {
+#pragma unroll
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
+        const f32x4 hout = dec * hin[j][pt] + hs[j][pt];
+        *reinterpret_cast<float4 *>(a.hT + (size_t)pair * PN + (size_t)p * N + n) =
+            make_float4(hout[0], hout[1], hout[2], hout[3]);
+      }
+  }
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
       const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
-      const f32x4 hout = dec * hin[j][pt] + hs[j][pt];
-      if (!tail) {
-        hcarry[j][pt] = hout;  // the next chunk of the segment starts from it
-      } else if (!last) {
-        ring_store4(rout, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16), hout);
-      } else if (a.hT) {
-        *reinterpret_cast<float4 *>(a.hT + (size_t)pair * PN + (size_t)p * N + n) =
-            make_float4(hout[0], hout[1], hout[2], hout[3]);
-      }
       uint2 hb;
       hb.x = pack2(hin[j][pt][0], hin[j][pt][1]);
       hb.y = pack2(hin[j][pt][2], hin[j][pt][3]);
@@ -617,6 +635,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   __syncthreads();  // ... and every other wave's; sH complete
   if (tail && !last && tid == 0)
     __hip_atomic_store(pub + pair, k.idx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tail) load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);
 
   // ---- 4. outputs, one 32-row tile at a time ------------------------------------
   // dt and x of the segment's next chunk (same sequence: a dense segment

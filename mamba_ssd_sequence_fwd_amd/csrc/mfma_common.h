@@ -45,9 +45,11 @@ __device__ __forceinline__ bf16x8 ldg8_row(const bf16 *base, size_t ld, int r, i
 }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  const bf16 a = (bf16)lo, b = (bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  // one vector conversion (v_cvt_pk_bf16_f32 takes both halves at once)
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Transposed staging of a token-major bf16 matrix (row stride `ld` elements,
