@@ -285,53 +285,93 @@ __device__ __forceinline__ f32x4 ring_load4(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice));
 }
 
-// Bounded wait until the published-chunk counter reaches `want`. Returns
-// false if the wall-clock limit ran out first.
-__device__ __forceinline__ bool wait_published(const int32_t *ctr, int want) {
-  constexpr uint64_t kLimitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
-  if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return true;
-  const uint64_t t0 = wall_clock64();
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
-    __builtin_amdgcn_s_sleep(2);
-    if (wall_clock64() - t0 > kLimitTicks) return false;
-  }
-  return true;
+// Per-(chunk, head) state slots in the workspace (the state leaving a chunk,
+// and a chunk's aggregate), in the state-tile layout of the waves (tile (j,
+// pt) of wave w: rows n = 16 (w NTW + j) + 4(lane/16) + r, column p = 16 pt
+// + lane%16), stored [wave][j][pt][lane][r]: one 16-byte access per lane and
+// 1 KB contiguous per wave access.
+__device__ __forceinline__ uint32_t slot_off(int wave, int ntw, int j, int pt, int lane) {
+  return (uint32_t)((((wave * ntw + j) * 4 + pt) * 64 + lane) * 16);
+}
+template <int N, int NTW>
+__device__ __forceinline__ void load_slot(f32x4 (&v)[NTW][4], const float *slot, int wave,
+                                          int lane) {
+  const __amdgpu_buffer_rsrc_t r = ring_rsrc(slot, kP * N * 4);
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) v[j][pt] = ring_load4(r, slot_off(wave, NTW, j, pt, lane));
 }
 
-// Incoming state of head h, chunk k, in the state-tile layout of this wave
-// (tile (j, pt): rows n = 16 (nt0 + j) + 4(lane/16) + r, column p = 16 pt +
-// lane%16): the ring slot of the previous chunk, or at a sequence start the
-// initial state (or zeros). Ring slot layout: [wave][j][pt][lane][r], one
-// 16-byte access per lane and 1 KB contiguous per wave access.
+// The initial state of head h of sequence s (or zeros), this wave's tiles.
 template <int N, int NTW>
-__device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, const Chunk &k,
-                                          int h, int wave, int nt0, int lane) {
-  const size_t PN = (size_t)kP * N;
+__device__ __forceinline__ void load_h0(f32x4 (&v)[NTW][4], const Args &a, int s, int h,
+                                        int nt0, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
-  if (k.idx > 0) {
-    const __amdgpu_buffer_rsrc_t rin = ring_rsrc(
-        a.ring + ((size_t)(k.seq * a.H + h) * 2 + ((k.idx + 1) & 1)) * PN, (int)(PN * 4));
-#pragma unroll
-    for (int j = 0; j < NTW; ++j)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-        hin[j][pt] = ring_load4(rin, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16));
-  } else if (a.h0) {
-    const float *h0 = a.h0 + (size_t)(k.seq * a.H + h) * PN;
+  if (a.h0) {
+    const float *h0 = a.h0 + (size_t)(s * a.H + h) * kP * N;
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
-        const float4 v = *reinterpret_cast<const float4 *>(h0 + (size_t)p * N + n);
-        hin[j][pt] = f32x4{v.x, v.y, v.z, v.w};
+        const float4 q = *reinterpret_cast<const float4 *>(h0 + (size_t)p * N + n);
+        v[j][pt] = f32x4{q.x, q.y, q.z, q.w};
       }
   } else {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) hin[j][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < 4; ++pt) v[j][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+}
+
+// The slot of the state leaving chunk number idx (global index c) of
+// sequence s, head h. With aggregates (kLook): one slot per (chunk, head),
+// never reused (a successor rebuilding its input may read it late).
+// Otherwise two per (sequence, head), by chunk parity: the state leaving
+// chunk i is read only by the unit of chunk i + 1, and the slot is next
+// written with the state leaving chunk i + 2, which needs that unit's result
+// first.
+template <int N, bool kLook>
+__device__ __forceinline__ float *inc_slot(const Args &a, int c, int idx, int s, int h) {
+  const size_t PN = (size_t)kP * N;
+  return kLook ? a.inc + ((size_t)c * a.H + h) * PN
+               : a.inc + ((size_t)(s * a.H + h) * 2 + (idx & 1)) * PN;
+}
+
+// Incoming state of chunk k (global index c), head h: the published state
+// leaving chunk c - 1, or at a sequence start the initial state.
+template <int N, int NTW, bool kLook>
+__device__ __forceinline__ void load_h_in(f32x4 (&hin)[NTW][4], const Args &a, const Chunk &k,
+                                          int c, int h, int wave, int nt0, int lane) {
+  if (k.idx > 0)
+    load_slot<N, NTW>(hin, inc_slot<N, kLook>(a, c - 1, k.idx - 1, k.seq, h), wave, lane);
+  else
+    load_h0<N, NTW>(hin, a, k.seq, h, nt0, lane);
+}
+
+// d h + S, one rounding per element: the state recurrence across a chunk
+// boundary, written out so that every place that evaluates it (the chunk's
+// own unit, a successor rebuilding it from the chunk's aggregate) gets the
+// same bits.
+__device__ __forceinline__ f32x4 step_state(float d, const f32x4 &h, const f32x4 &S) {
+  return f32x4{__builtin_fmaf(d, h[0], S[0]), __builtin_fmaf(d, h[1], S[1]),
+               __builtin_fmaf(d, h[2], S[2]), __builtin_fmaf(d, h[3], S[3])};
+}
+
+// Bounded wait until a status word is nonzero; its value, or 0 if the
+// wall-clock limit ran out first.
+__device__ __forceinline__ int wait_status(const int32_t *st) {
+  constexpr uint64_t kLimitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
+  int v = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (v != 0) return v;
+  const uint64_t t0 = wall_clock64();
+  while ((v = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+    __builtin_amdgcn_s_sleep(2);
+    if (wall_clock64() - t0 > kLimitTicks) return 0;
+  }
+  return v;
 }
 
 // kDeep: every B^T tile of step 2 is loaded up front instead of four steps
@@ -379,11 +419,12 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   __shared__ __attribute__((aligned(16))) float sU[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];
   __shared__ float sTot[4];
-  __shared__ int sTicket, sReady;
+  __shared__ int sTicket, sReady, sNb;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int32_t *ticket = a.sync, *err = a.sync + 1, *pub = a.sync + kSyncHeader;
+  int32_t *ticket = a.sync, *err = a.sync + 1, *stat = a.sync + kSyncHeader;
+  int32_t *decw = stat + (size_t)a.nc_max * a.H;  // log2 decay of each published aggregate
 
   // ---- work unit: (first chunk, head, chunks in the segment) -----------------
   if (tid == 0) sTicket = atomicAdd(ticket, 1);
@@ -470,9 +511,10 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
                                 : static_cast<const bf16 *>(a.dt)[(size_t)(k.start + min(tid, k.len - 1)) * a.H + h];
   const int pair = k.seq * a.H + h;
   const bool first = k.idx == 0;
-  int early = 0;  // published count of the predecessor, read early
+  int early = 0;  // the predecessor's status, read early
   if (head && !first && tid == 0)
-    early = __hip_atomic_load(pub + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    early = __hip_atomic_load(stat + (size_t)(c - 1) * a.H + h, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
   const int nt0 = wave * NTW;
   // This wave's B^T operand tiles (n tiles nt0..), streamed KPF 32-token
   // steps ahead of their use; the first KPF steps now.
@@ -502,7 +544,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   };
   const float incl = wave_inclusive_sum(dtv * ah);
   if (lane == 63 && wave < Q / 64) sTot[wave] = incl;
-  if (head && tid == 0) sReady = (first || early >= k.idx) ? 1 : 0;
+  if (head && tid == 0) sReady = (first || early == kIncReady) ? 1 : 0;
   __syncthreads();
   float pre = 0.f, cs_last = 0.f;
 #pragma unroll
@@ -533,7 +575,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) hin[j][pt] = hcarry[j][pt];
   } else if (ready) {
-    load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
+    load_h_in<N, NTW, kDeep>(hin, a, k, c, h, wave, nt0, lane);
   }
   f32x4 hs[NTW][4];
 #pragma unroll
@@ -581,17 +623,95 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- 3. h_in; h_out = 2^(cs_last) h_in + S_c to the ring; publish ------------
+  // ---- 3. h_in; h_out = 2^(cs_last) h_in + S_c published; ----------------------
   const int iA = wave, iB = T - 1 - wave;
-  if (!ready) {
-    if (tid == 0 && !wait_published(pub + pair, k.idx))
+  if (!ready && !kDeep) {
+    // The state leaving the previous chunk was not published before S_c:
+    // wait for it (these units publish nothing else).
+    if (tid == 0 && wait_status(stat + (size_t)(c - 1) * a.H + h) != kIncReady)
       __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    load_h_in<N, NTW>(hin, a, k, h, wave, nt0, lane);
+    load_h_in<N, NTW, false>(hin, a, k, c, h, wave, nt0, lane);
+  } else if (!ready) {
+    // kDeep (every unit resident at once): rather than wait for the
+    // predecessor's own wait, publish this chunk's aggregate (S_c and its
+    // decay) if that state is still missing, then rebuild h_in from the
+    // nearest predecessor whose leaving state is published (or the sequence
+    // start) and the aggregates of the chunks after it: h = 2^(d_m) h + S_m,
+    // chunk by chunk, the very evaluation each of those units performs, so
+    // h_in has the bits the plain chain would give it.
+    if (tid == 0)  // (every wave read sReady before S_c)
+      sReady = __hip_atomic_load(stat + (size_t)(c - 1) * a.H + h, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sReady != kIncReady) {
+      const __amdgpu_buffer_rsrc_t r = ring_rsrc(a.agg + ((size_t)c * a.H + h) * PN, (int)(PN * 4));
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) ring_store4(r, slot_off(wave, NTW, j, pt, lane), hs[j][pt]);
+      if (tid == 0)
+        __hip_atomic_store(decw + (size_t)c * a.H + h, __float_as_int(cs_last), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      wait_vmem_all();  // this wave's stores have completed (device-coherent)
+      __syncthreads();  // ... and every other wave's
+      if (tid == 0)
+        __hip_atomic_store(stat + (size_t)c * a.H + h, kAggReady, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Wave 0 reads the status of up to 64 predecessors at once (lane i:
+    // chunk c - 1 - i) until the nearest published leaving state (or the
+    // sequence start, when within reach) has only published aggregates after
+    // it; sNb = how many chunks to rebuild from aggregates.
+    if (wave == 0) {
+      constexpr uint64_t kLimitTicks = 100000000ull;  // 1 s of the 100 MHz constant clock
+      const int m = min(64, k.idx);
+      const uint64_t t0 = wall_clock64();
+      int nb = 0;
+      for (;;) {
+        const int v = lane < m ? __hip_atomic_load(stat + (size_t)(c - 1 - lane) * a.H + h,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0;
+        const uint64_t incm = __ballot(lane < m && v == kIncReady);
+        const uint64_t aggm = __ballot(lane < m && v != 0);
+        // the base: the nearest published leaving state, else the start
+        const int b = incm ? __builtin_ctzll(incm) : (k.idx <= 64 ? m : -1);
+        const uint64_t need = b >= 64 ? ~0ull : ((1ull << b) - 1);
+        if (b >= 0 && (aggm & need) == need) {
+          nb = b;
+          break;
+        }
+        if (wall_clock64() - t0 > kLimitTicks) {  // flagged; the outputs are then wrong
+          if (lane == 0) __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          nb = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (lane == 0) sNb = nb;
+    }
+    __syncthreads();
+    const int nb = sNb;
+    if (nb < k.idx) {
+      load_slot<N, NTW>(hin, inc_slot<N, true>(a, c - 1 - nb, k.idx - 1 - nb, k.seq, h), wave, lane);
+    } else {
+      load_h0<N, NTW>(hin, a, k.seq, h, nt0, lane);
+    }
+#pragma unroll 1
+    for (int q = c - nb; q < c; ++q) {
+      f32x4 t[NTW][4];
+      load_slot<N, NTW>(t, a.agg + ((size_t)q * a.H + h) * PN, wave, lane);
+      const float d = exp2_fast(__int_as_float(
+          __hip_atomic_load(decw + (size_t)q * a.H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) hin[j][pt] = step_state(d, hin[j][pt], t[j][pt]);
+    }
   }
   const bool last = k.last;
   const float dec = exp2_fast(cs_last);
-  // The C rows of the first output tile: issued now only when no ring store
+  // The C rows of the first output tile: issued now only when no state store
   // follows (the wait for the stores would wait for them too), else after
   // the publish.
   bf16x8 acA[2][N / 32];
@@ -600,23 +720,22 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) hcarry[j][pt] = dec * hin[j][pt] + hs[j][pt];
+      for (int pt = 0; pt < 4; ++pt) hcarry[j][pt] = step_state(dec, hin[j][pt], hs[j][pt]);
   } else if (!last) {
     const __amdgpu_buffer_rsrc_t rout =
-        ring_rsrc(a.ring + ((size_t)pair * 2 + (k.idx & 1)) * PN, (int)(PN * 4));
+        ring_rsrc(inc_slot<N, kDeep>(a, c, k.idx, k.seq, h), (int)(PN * 4));
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-        ring_store4(rout, (uint32_t)((((wave * NTW + j) * 4 + pt) * 64 + lane) * 16),
-                    dec * hin[j][pt] + hs[j][pt]);
+        ring_store4(rout, slot_off(wave, NTW, j, pt, lane), step_state(dec, hin[j][pt], hs[j][pt]));
   } else if (a.hT) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         const int n = 16 * (nt0 + j) + 4 * lg, p = 16 * pt + lr;
-        const f32x4 hout = dec * hin[j][pt] + hs[j][pt];
+        const f32x4 hout = step_state(dec, hin[j][pt], hs[j][pt]);
         *reinterpret_cast<float4 *>(a.hT + (size_t)pair * PN + (size_t)p * N + n) =
             make_float4(hout[0], hout[1], hout[2], hout[3]);
       }
@@ -631,10 +750,11 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
       hb.y = pack2(hin[j][pt][2], hin[j][pt][3]);
       *reinterpret_cast<uint2 *>(sH + swz<N>(p, n)) = hb;
     }
-  if (tail) wait_vmem_all();  // this wave's ring stores have completed (device-coherent)
+  if (tail) wait_vmem_all();  // this wave's state stores have completed (device-coherent)
   __syncthreads();  // ... and every other wave's; sH complete
   if (tail && !last && tid == 0)
-    __hip_atomic_store(pub + pair, k.idx + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(stat + (size_t)c * a.H + h, kIncReady, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   if (tail) load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);
 
   // ---- 4. outputs, one 32-row tile at a time ------------------------------------
@@ -778,6 +898,12 @@ int64_t chain_units(const Args &a) {
   if (!a.varlen) return (int64_t)a.nseq * ((a.nc_per + s - 1) / s) * a.H;
   // sum over sequences of ceil(chunks / s) <= (chunks + sequences (s - 1)) / s
   return (((int64_t)a.nc_max + (int64_t)a.nseq * (s - 1)) / s) * a.H;
+}
+
+// Whether the launch takes the kDeep kernel, whose units publish aggregates
+// and the state leaving every chunk (one slot each).
+bool chain_lookback(const Args &a) {
+  return a.N != 256 && a.seg <= 1 && chain_units(a) <= kDeepMaxUnits;
 }
 
 template <int N, int Q>

@@ -64,8 +64,10 @@ enum Path {
 struct Layout {
   int64_t nc_max;
   int64_t rec_off;  // int32 offset of the chunk records in the plan area
-  size_t plan, cs, states, cb, bt, zeros, sync, ring, total;
-  int64_t nsync;
+  size_t plan, cs, states, cb, bt, zeros, sync, inc, agg, total;
+  int64_t nsync;     // int32 words of the chained kernel's sync area
+  int64_t nzero;     // ... of which the C B^T kernel zeroes the first nzero
+  int seg;           // chained kernel: chunks per work unit
   Path path;
   bool mfma;
 };
@@ -118,13 +120,35 @@ Layout make_layout(const ssd_problem &p) {
   L.zeros = off;
   if (L.mfma) off += kAlign;
   const int64_t nseq = p.num_seqs > 0 ? p.num_seqs : p.batch;
+  // chained kernel: a status word and a decay per (chunk, head), the state
+  // leaving every chunk, and (one-chunk units) every chunk's aggregate
+  const bool chain = L.path == kMfmaChain && L.nc_max > 0;
+  L.seg = 1;
+  bool look = false;  // units publish aggregates (one state slot per chunk)
+  if (chain) {
+    ssd::Args a{};
+    a.N = p.dstate;
+    a.H = p.nheads;
+    a.varlen = p.num_seqs > 0 ? 1 : 0;
+    a.nseq = (int32_t)nseq;
+    a.nc_per = a.varlen ? 0 : (p.seqlen + p.chunk_size - 1) / p.chunk_size;
+    a.nc_max = (int32_t)L.nc_max;
+    L.seg = a.seg = ssd::chain_segment(a);
+    look = ssd::chain_lookback(a);
+  }
+  const size_t state_bytes = (size_t)p.headdim * p.dstate * sizeof(float);
+  const size_t per_chunk = (size_t)L.nc_max * p.nheads * state_bytes;
   L.sync = off;
-  L.nsync = (L.path == kMfmaChain && L.nc_max > 0) ? ssd::kSyncHeader + nseq * p.nheads : 0;
+  L.nzero = chain ? ssd::kSyncHeader + L.nc_max * p.nheads : 0;
+  L.nsync = chain ? L.nzero + L.nc_max * p.nheads : 0;
   off = round_up(off + (size_t)L.nsync * sizeof(int32_t), kAlign);
-  L.ring = off;
-  if (L.nsync > 0)
-    off = round_up(off + (size_t)nseq * p.nheads * 2 * p.headdim * p.dstate * sizeof(float),
-                   kAlign);
+  // the state leaving a chunk: two slots per (sequence, head), or with
+  // aggregates one per (chunk, head), then the aggregates
+  L.inc = off;
+  if (chain)
+    off = round_up(off + (look ? per_chunk : (size_t)nseq * p.nheads * 2 * state_bytes), kAlign);
+  L.agg = off;
+  if (look) off = round_up(off + per_chunk, kAlign);
   L.total = off;
   return L;
 }
@@ -200,8 +224,9 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.zeros = ws + L.zeros;
   a.bt = L.path == kMfmaChain ? ws + L.bt : nullptr;
   a.sync = reinterpret_cast<int32_t *>(ws + L.sync);
-  a.ring = reinterpret_cast<float *>(ws + L.ring);
-  a.nsync = (int32_t)L.nsync;
+  a.inc = reinterpret_cast<float *>(ws + L.inc);
+  a.agg = L.agg < L.total ? reinterpret_cast<float *>(ws + L.agg) : nullptr;
+  a.nsync = (int32_t)L.nzero;
   a.batch = p->batch;
   a.L = p->seqlen;
   a.H = p->nheads;
@@ -217,7 +242,7 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.rec_off = (int32_t)L.rec_off;
   a.order_off = (int32_t)(L.rec_off + 4 * L.nc_max);
   a.nseg_off = varlen ? 3 + p->num_seqs : 0;
-  a.seg = L.path == kMfmaChain ? ssd::chain_segment(a) : 1;
+  a.seg = L.path == kMfmaChain ? L.seg : 1;
   a.nrange = L.path == kMfmaChain ? ssd::chain_ranges(a, device_compute_units()) : 0;
   return a;
 }
@@ -566,7 +591,7 @@ ssd_status ssd_validate(const ssd_problem *p) {
   const int64_t sp_blocks = (int64_t)((p->headdim * p->dstate / 4 + 255) / 256) * p->nheads * nseq;
   const Layout L = make_layout(*p);
   if (sp_blocks > INT32_MAX || L.nc_max * 5 + L.rec_off > INT32_MAX ||
-      L.nc_max * p->nheads > INT32_MAX)
+      L.nc_max * p->nheads > INT32_MAX || L.nsync > INT32_MAX)
     return fail(SSD_ERR_UNSUPPORTED, "problem too large for 32-bit grid indexing");
   return SSD_OK;
 }

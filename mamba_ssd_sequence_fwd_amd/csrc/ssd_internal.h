@@ -28,9 +28,15 @@ struct Args {
   void *cb;             // bf16 C B^T tiles (MFMA path only)
   void *zeros;          // 256 zero bytes (written by the C B^T kernel)
   void *bt;             // chain path: bf16 B^T operand tiles per (chunk, group), or null
-  int32_t *sync;        // chain path: [0] ticket, [1] error word, [kSyncHeader + seq*H + h]
-                        // published-chunk counters; zeroed by the C B^T kernel
-  float *ring;          // chain path: (S, H, 2, P, N) fp32 state hand-off ring
+  int32_t *sync;        // chain path: [0] ticket, [1] error word, [kSyncHeader + c*H + h]
+                        // status of chunk c, head h (kAggReady / kIncReady), then the
+                        // chunk's log2 decay as float bits at [kSyncHeader + nc_max*H +
+                        // c*H + h]; the first kSyncHeader + nc_max*H ints are zeroed by
+                        // the C B^T kernel
+  float *inc;           // chain path: (chunks, H, P, N) fp32 state leaving each chunk
+  float *agg;           // chain path, one-chunk units: (chunks, H, P, N) fp32 state each
+                        // chunk builds from a zero start, published when its
+                        // predecessor's was late (null otherwise)
   int32_t nsync;        // ints of `sync` to zero (0 off the chain path)
   int32_t batch, L, H, P, N, G, Q;
   int32_t nseq;         // sequences: batch (dense) or num_seqs (varlen)
@@ -48,8 +54,11 @@ struct Args {
                         // nrange balanced ranges of the (sequence, head, chunk) order
 };
 
-// Ints ahead of the per-(sequence, head) counters in Args::sync.
+// Ints ahead of the per-(chunk, head) status words in Args::sync, and the
+// status values: the chunk's aggregate (its own state from a zero start and
+// its decay) is published, or the state leaving it is.
 constexpr int kSyncHeader = 64;
+constexpr int kAggReady = 1, kIncReady = 2;
 
 // Packed sequences up to which the plan orders the chained kernel's work
 // units by their index inside the sequence (above it: sequence by sequence,
@@ -206,6 +215,7 @@ bool chain_path_supports(const Args &a);
 hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream_t s);
 int chain_segment(const Args &a);
 int chain_ranges(const Args &a, int compute_units);
+bool chain_lookback(const Args &a);
 bool f32seq_path_supports(const Args &a);
 hipError_t launch_f32seq(const Args &a, hipStream_t s);
 hipError_t launch_final_of_empty(const Args &a, hipStream_t s);

@@ -118,14 +118,18 @@ def test_workspace_layout_varlen_bound(lib):
 
 
 def test_workspace_layout_chain_counters(lib):
-    """The default bf16 path (chained workgroups) has one counter per
-    (sequence, head) after a 64-word header; the other paths have none."""
+    """The default bf16 path (chained workgroups) has a status word and a
+    decay word per (chunk, head) after a 64-word header, then the state
+    leaving every chunk and (one-chunk units) every chunk's aggregate, fp32
+    P x N each; the other paths have none."""
     lay = ssd.workspace_layout(P())
-    assert lay.chain_sync_words == 64 + 2 * 8 and lay.chain_sync % 256 == 0
+    nc = 2 * 4                                   # batch 2, ceil(1000/256) = 4
+    assert lay.chain_sync_words == 64 + 2 * nc * 8 and lay.chain_sync % 256 == 0
+    assert lay.chain_chunks_per_unit == 1        # 64 units: one chunk each, aggregates kept
     assert ssd.workspace_size(P()) >= lay.chain_sync + 4 * lay.chain_sync_words + \
-        2 * 8 * 2 * 64 * 128 * 4
+        2 * nc * 8 * 64 * 128 * 4
     lay_v = ssd.workspace_layout(P(batch=1, seqlen=5000, num_seqs=7))
-    assert lay_v.chain_sync_words == 64 + 7 * 8
+    assert lay_v.chain_sync_words == 64 + 2 * (5000 // 256 + 7) * 8
     for flags in (ssd.SSD_FLAG_UNFUSED, ssd.SSD_FLAG_PER_SEQUENCE, ssd.SSD_FLAG_GENERIC_KERNELS):
         assert ssd.workspace_layout(P(flags=flags)).chain_sync_words == 0
 
@@ -134,11 +138,12 @@ def test_workspace_grows_with_problem(lib):
     a = ssd.workspace_size(P(seqlen=1000))
     b = ssd.workspace_size(P(seqlen=2000))
     assert b > a
-    # generic kernels need no C.B^T buffer; the fused kernel keeps the
-    # per-chunk states on chip
+    # generic kernels need no C.B^T buffer; the per-sequence fused kernel
+    # keeps the per-chunk states on chip (the chained kernel publishes the
+    # state leaving every chunk, and one-chunk units every chunk's aggregate)
     unf = ssd.workspace_size(P(flags=ssd.SSD_FLAG_UNFUSED))
     assert ssd.workspace_size(P(flags=ssd.SSD_FLAG_GENERIC_KERNELS)) < unf
-    assert a < unf
+    assert ssd.workspace_size(P(flags=ssd.SSD_FLAG_PER_SEQUENCE)) < unf
 
 
 def test_forward_rejects_bad_arguments_before_launch(lib):
