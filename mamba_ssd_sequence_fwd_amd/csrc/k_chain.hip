@@ -1,46 +1,53 @@
 // k_chain.hip -- the chunked SSD forward pass with one workgroup per
-// (chunk, head), the inter-chunk recurrence carried by a chain of
-// workgroups (bf16 inputs, MFMA, fp32 state).
+// (chunk, head) or per run of consecutive chunks, the inter-chunk
+// recurrence carried between workgroups (bf16 inputs, MFMA, fp32 state).
 //
 // The SSD layer evaluates the semiseparable matrix by blocks: inside a chunk
 // a masked-attention product, across chunks a linear recurrence on one state
 // per chunk (QbitAI "Mamba-2" article, srwj168 repost, sections "Unifying SSM
 // and attention" and "Mamba-2: stronger learning, faster training and
-// inference"). Every (chunk, head) is an independent workgroup; only the
-// recurrence h_out = 2^(cs_last) h_in + S_c links the chunks of one
-// (sequence, head), and it is handed from the workgroup of chunk j to that
-// of chunk j+1 through a two-slot fp32 ring in device memory plus a
-// published-chunk counter. Per workgroup (four waves), with cs the log2-decay
-// prefix of dt*A inside the chunk:
+// inference"). Only the recurrence h_out = 2^(cs_last) h_in + S_c links the
+// chunks of one (sequence, head); the workgroup of a chunk publishes the
+// state leaving it in device memory and sets the chunk's status word, and
+// the workgroup of the next chunk reads it. Per chunk (four waves), with cs
+// the log2-decay prefix of dt*A inside the chunk:
 //
-//   1. ticket -> (chunk, head); dt, the chunk's first B^T operand tiles and
-//      x into registers (loads complete in issue order, so x is waited for
-//      step by step); the decay tables (cs, w, u) by a wavefront prefix; the
-//      first half of x into LDS (the second half halfway through step 2).
+//   1. ticket -> work unit; dt, the chunk's first B^T operand tiles and x
+//      into registers (every load issued before any is waited for; loads
+//      complete in issue order, so x is waited for step by step); the decay
+//      tables (cs, w, u) by a wavefront prefix; the first half of x into LDS
+//      (the second half halfway through step 2).
 //   2. S_c = (w o B)^T x (w_s = 2^(cs_last - cs_s) dt_s): the chunk's own
 //      state from a zero start (the chunk_state step).
-//   3. h_in from the previous chunk's workgroup (loaded while step 2 runs when
-//      it is already published), or the initial state / zero at a sequence
-//      start; h_out = 2^(cs_last) h_in + S_c goes to the ring (or to the final
-//      state after the sequence's last chunk) and is published (the
-//      state_passing step).
+//   3. h_in: the previous chunk's published state (loaded while step 2 runs
+//      when it is already there), the state carried in registers inside a
+//      run, or the initial state / zero at a sequence start; h_out =
+//      2^(cs_last) h_in + S_c is published (or kept for the run's next
+//      chunk, or written as the final state) (the state_passing step).
 //   4. outputs, per 32-row tile: (C B^T o decay mask)(dt o x) + D x with the
 //      C B^T tiles precomputed once per (chunk, group), plus 2^(cs_l) C_l h_in^T
 //      (the chunk_scan step); y.
 //
-// For dense problems with more units than the chip holds, a work unit is a
-// segment of up to four consecutive chunks of one (sequence, head), walked by
-// one workgroup with the state passed between them in registers (kSeg below),
-// so only every fourth chunk boundary goes through the ring.
+// Work units, chosen by the launcher from the grid size:
+//   - problems the chip holds at once (kDeep): one chunk each; a unit whose
+//     predecessor's state is late publishes its own aggregate (S_c and its
+//     decay) and rebuilds h_in from the nearest published state and the
+//     aggregates after it (the chunk maps compose associatively), so no unit
+//     waits for its predecessor's own wait;
+//   - dense problems with more units than that (kSeg): runs of consecutive
+//     chunks of one (sequence, head) with the state carried in registers,
+//     either segments of four chunks or, with at least one pair per resident
+//     workgroup, one balanced range of the (sequence, head, chunk) order per
+//     workgroup, so only range or segment boundaries go through memory;
+//   - everything else (packed input, N = 256): one chunk each.
 //
-// Tickets from an atomic counter order the work units by chunk index inside
-// the sequence, then sequence, then head, so the predecessor of a unit took
-// its ticket a whole chunk-index level earlier and has normally published by
-// the time step 3 asks. A workgroup only ever waits on a smaller ticket, i.e.
-// on one that is already running, so the chain cannot deadlock whatever order
-// the hardware dispatches in. Every wait is bounded by a wall-clock limit; a
-// wait that runs out sets an error word instead of hanging (the outputs are
-// then wrong).
+// Tickets from an atomic counter order the work units so that a unit's
+// predecessors took smaller tickets. A workgroup only ever waits on a
+// smaller ticket, i.e. on one that is already running, and every unit
+// publishes without waiting on a larger one, so the chain cannot deadlock
+// whatever order the hardware dispatches in. Every wait is bounded by a
+// wall-clock limit; a wait that runs out sets an error word instead of
+// hanging (the outputs are then wrong).
 //
 // LDS holds only x (the operand both products read transposed) and h_in
 // (bf16), 52 KB at chunk 256, so three workgroups share a CU. Each wave owns
@@ -53,7 +60,8 @@
 // arithmetic (LDS returns in order).
 //
 // HBM traffic: x, y once; B, C, dt and the C B^T tiles once per head
-// through L2; 32 KB of fp32 state written and read per (work unit, head).
+// through L2; 32 KB of fp32 state written and read per hand-off (N = 128),
+// plus 32 KB per published aggregate.
 #include "mfma_common.h"
 
 namespace ssd {
@@ -375,12 +383,16 @@ __device__ __forceinline__ int wait_status(const int32_t *st) {
 }
 
 // kDeep: every B^T tile of step 2 is loaded up front instead of four steps
-// ahead, at two workgroups per CU instead of three (more registers). When a
-// problem has no more work units than the chip holds at once, each
-// workgroup's own latency is the whole time and this wins (config-1 shapes:
-// 66 -> 56 us); with many units per slot the third workgroup per CU hides
-// that latency better (the 2.7B shapes: equal; long packed input: 13%
-// slower), so the launcher picks it by grid size.
+// ahead, at two workgroups per CU instead of three (more registers), and
+// units publish aggregates (one state slot per chunk). When a problem has no
+// more work units than the chip holds at once, each workgroup's own latency
+// is the whole time and this wins (config-1 shapes: 66 -> 56 us, then 57.0
+// -> 51.2 us with aggregates; the same aggregates with three workgroups per
+// CU and four-step prefetch: 56.3 us); with many units per slot the third
+// workgroup per CU hides that latency better (the 2.7B shapes: equal; long
+// packed input: 13% slower), and aggregates there cost more than they save
+// (N = 256 long sequences: 592 -> 662 us), so the launcher picks it by grid
+// size.
 //
 // kSeg: a work unit is a segment of up to a.seg consecutive chunks of one
 // (sequence, head), walked in order by the same workgroup. Inside a segment
