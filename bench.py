@@ -39,14 +39,17 @@ COLD_EVICT_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
 MFMA_FP32_PEAK_TFLOPS = 157.3
 
 
-def algorithmic_cost(w: si.Workload, inp: dict, chunks_per_unit: int = 1) -> dict:
+def algorithmic_cost(w: si.Workload, inp: dict, chunks_per_unit: int = 1, ranges: int = 0) -> dict:
     """Bytes each kernel must move and flops it must do, by the method's
     definition (unique HBM bytes; causal pairs only; C B^T once per group).
 
     Per (chunk, head) unit with q tokens: x q*P*e, y q*P*e, dt q*e, state
     P*N*4 (fp32), cumsum q*4; per (chunk, group): B and C q*N*e each.
     ``chunks_per_unit``: consecutive chunks the chained kernel's workgroups
-    walk with the state on chip (the hand-off overhead is between units).
+    walk with the state on chip (the hand-off overhead is between units);
+    ``ranges`` > 0: its workgroups take that many balanced ranges of the
+    (sequence, head, chunk) order instead, handing off where a range starts
+    inside a sequence (dense input).
     """
     e = 2 if w.dtype == "bf16" else 4
     lens = inp["seq_lens"] or [w.seqlen] * w.batch
@@ -78,6 +81,17 @@ def algorithmic_cost(w: si.Workload, inp: dict, chunks_per_unit: int = 1) -> dic
     k = max(1, chunks_per_unit)
     units = sum(((L + Q - 1) // Q + k - 1) // k for L in lens)
     handoff = 2 * (units - sum(1 for L in lens if L > 0)) * H * state
+    if ranges > 0:
+        # one queue of ranges per XCD, each over an eighth of the (sequence,
+        # head) pairs; a range starting inside a sequence takes a hand-off
+        per = (lens[0] + Q - 1) // Q            # dense: chunks of every sequence
+        pairs, nq = len(lens) * H, 8
+        rq = ranges // nq
+        n = 0
+        for q in range(nq):
+            units = (pairs * (q + 1) // nq - pairs * q // nq) * per
+            n += sum(1 for t in range(1, rq) if (t * units // rq) % per)
+        handoff = 2 * state * n
     cost["ssd_chain"] = dict(bytes=cost["ssd_fused"]["bytes"], flops=cost["ssd_fused"]["flops"],
                              overhead_bytes=handoff)
     # fp32 problems: one workgroup per (sequence, head), no C B^T tiles
@@ -569,7 +583,8 @@ def main():
               file=sys.stderr)
         sys.exit(3)
 
-    cost = algorithmic_cost(w, inp, int(plan.layout().chain_chunks_per_unit))
+    lay = plan.layout()
+    cost = algorithmic_cost(w, inp, int(lay.chain_chunks_per_unit), int(lay.chain_ranges))
     kernels = {}
     for name, ms in per_kernel_ms.items():
         c = cost.get(name, {"bytes": 0, "flops": 0})

@@ -257,6 +257,14 @@ typedef struct ssd_workspace_layout {
                                passing the state between them on chip; the
                                state goes through the workspace only between
                                such units (0 = no chained kernel) */
+  int64_t chain_ranges;     /* > 0: the chained kernel's workgroups each take
+                               one of this many balanced ranges of the
+                               (sequence, head, chunk) order instead (dense
+                               input with at least as many (sequence, head)
+                               pairs as the current device holds such
+                               workgroups); the state goes through the
+                               workspace where a range starts inside a
+                               sequence */
 } ssd_workspace_layout;
 ssd_status ssd_get_workspace_layout(const ssd_problem *prob,
                                     ssd_workspace_layout *layout);

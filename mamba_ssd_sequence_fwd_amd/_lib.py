@@ -44,7 +44,8 @@ class WorkspaceLayout(ctypes.Structure):
     _fields_ = [("chunk_cumsum", ctypes.c_size_t), ("chunk_states", ctypes.c_size_t),
                 ("chunk_table", ctypes.c_size_t), ("chunk_records", ctypes.c_int64),
                 ("max_chunks", ctypes.c_int64), ("chain_sync", ctypes.c_size_t),
-                ("chain_sync_words", ctypes.c_int64), ("chain_chunks_per_unit", ctypes.c_int64)]
+                ("chain_sync_words", ctypes.c_int64), ("chain_chunks_per_unit", ctypes.c_int64),
+                ("chain_ranges", ctypes.c_int64)]
 
 
 class ScanProblem(ctypes.Structure):

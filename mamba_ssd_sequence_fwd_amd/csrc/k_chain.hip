@@ -403,16 +403,18 @@ __device__ __forceinline__ int wait_status(const int32_t *st) {
 // registers (N = 128), so segments run two workgroups per CU.
 //
 // kSeg with a.nrange > 0 (dense input with at least as many (sequence, head)
-// pairs as the chip holds workgroups): instead of equal segments, workgroup
-// k takes the k-th of a.nrange balanced ranges of the chunk order (sequence,
-// head, chunk index), so that every workgroup walks the same number of
-// chunks and none is left for a partial last wave. A range holds at least
-// one pair's worth of chunks, so it is a run of whole pairs with at most a
-// partial pair at each end: one that continues the previous range's last
-// pair and one that the next range continues. The workgroup walks its last
-// part first (it starts at a pair's first chunk and waits on nothing), then
-// the whole pairs, then the first part, whose predecessor the previous
-// workgroup (a smaller ticket) walked first.
+// pairs as the chip holds workgroups): instead of equal segments, each
+// workgroup takes one of a.nrange balanced ranges of the chunk order
+// (sequence, head, chunk index), so that every workgroup walks the same
+// number of chunks and none is left for a partial last wave. The ranges come
+// from one queue per XCD, each over an eighth of the pairs, so that the
+// workgroups of one L2 read the same B, C and C B^T tiles. A range holds at
+// least one pair's worth of chunks, so it is a run of whole pairs with at
+// most a partial pair at each end: one that continues the previous range of
+// its queue and one that the next range continues. The workgroup walks its
+// last part first (it starts at a pair's first chunk and waits on nothing),
+// then the whole pairs, then the first part, whose predecessor the workgroup
+// of the previous range (taken earlier from the same queue) walked first.
 template <int N, int Q, bool kDeep, bool kSeg>
 __global__ __launch_bounds__(64 * kChainWaves)
 __attribute__((amdgpu_waves_per_eu(N == 256 || kDeep || kSeg ? 2 : 3,
@@ -439,15 +441,39 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   int32_t *decw = stat + (size_t)a.nc_max * a.H;  // log2 decay of each published aggregate
 
   // ---- work unit: (first chunk, head, chunks in the segment) -----------------
-  if (tid == 0) sTicket = atomicAdd(ticket, 1);
+  if (tid == 0) {
+    if (kSeg && a.nrange > 0) {
+      // range mode: a queue of ranges per XCD, over a contiguous block of
+      // (sequence, head) pairs, so that the workgroups sharing an L2 read
+      // the same B, C and C B^T tiles; an XCD whose queue is used up takes
+      // from the next ones. Each queue is taken in order, and a range waits
+      // only on the one before it in its queue.
+      unsigned x;
+      asm volatile("s_getreg_b32 %0, hwreg(20, 0, 4)" : "=s"(x));  // XCC_ID
+      const int per = a.nrange / kRangeQueues;
+      int got = -1;
+      for (int d = 0; d < kRangeQueues && got < 0; ++d) {
+        const int q = (int)((x + d) % kRangeQueues);
+        const int t = atomicAdd(a.sync + kRangeQueueWord + q, 1);
+        if (t < per) got = q * per + t;
+      }
+      sTicket = got;
+    } else {
+      sTicket = atomicAdd(ticket, 1);
+    }
+  }
   __syncthreads();
   const int tk = sTicket;
   int c0 = 0, h = 0, nk = 1;
   int64_t rlo = 0, rhi = 0;  // range mode: [rlo, rhi) of the (sequence, head, chunk) order
   if (kSeg && a.nrange > 0) {
-    const int64_t units = (int64_t)a.nseq * a.H * a.nc_per;
-    rlo = (int64_t)tk * units / a.nrange;
-    rhi = (int64_t)(tk + 1) * units / a.nrange;
+    if (tk < 0) return;  // (every workgroup finds a range: as many ranges as workgroups)
+    const int per = a.nrange / kRangeQueues, q = tk / per, t = tk - q * per;
+    const int64_t pairs = (int64_t)a.nseq * a.H;
+    const int64_t p0 = q * pairs / kRangeQueues, p1 = (q + 1) * pairs / kRangeQueues;
+    const int64_t u0 = p0 * a.nc_per, units = (p1 - p0) * a.nc_per;
+    rlo = u0 + t * units / per;
+    rhi = u0 + (t + 1) * units / per;
   } else if (!a.varlen) {
     const int per = a.nseq * a.H;
     const int j = tk / per, r = tk - j * per, s = r / a.H;
@@ -899,7 +925,8 @@ constexpr int kSegWorkgroupsPerCu = 2;
 // bit-identical.
 int chain_ranges(const Args &a, int compute_units) {
   if (a.varlen || a.N == 256 || a.seg <= 1 || a.nc_per < 2) return 0;
-  const int64_t slots = (int64_t)compute_units * kSegWorkgroupsPerCu;
+  // a whole number of ranges per queue
+  const int64_t slots = (int64_t)compute_units * kSegWorkgroupsPerCu / kRangeQueues * kRangeQueues;
   if (slots <= 0 || (int64_t)a.nseq * a.H < slots) return 0;
   return (int)slots;
 }

@@ -643,6 +643,7 @@ ssd_status ssd_get_workspace_layout(const ssd_problem *p, ssd_workspace_layout *
   out->chain_sync = L.nsync ? L.sync : 0;
   out->chain_sync_words = L.nsync;
   out->chain_chunks_per_unit = 0;
+  out->chain_ranges = 0;
   if (L.nsync) {
     ssd::Args a{};
     a.N = p->dstate;
@@ -653,8 +654,8 @@ ssd_status ssd_get_workspace_layout(const ssd_problem *p, ssd_workspace_layout *
     a.nc_max = (int32_t)L.nc_max;
     a.seg = ssd::chain_segment(a);
     // balanced ranges walk whole sequences of chunks
-    out->chain_chunks_per_unit =
-        ssd::chain_ranges(a, device_compute_units()) > 0 ? a.nc_per : a.seg;
+    out->chain_ranges = ssd::chain_ranges(a, device_compute_units());
+    out->chain_chunks_per_unit = out->chain_ranges > 0 ? a.nc_per : a.seg;
   }
   return SSD_OK;
 }

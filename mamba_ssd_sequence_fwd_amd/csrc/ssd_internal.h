@@ -59,6 +59,9 @@ struct Args {
 // its decay) is published, or the state leaving it is.
 constexpr int kSyncHeader = 64;
 constexpr int kAggReady = 1, kIncReady = 2;
+// Range mode of the chained kernel: one queue of ranges per XCD, whose
+// counters are Args::sync[kRangeQueueWord + q].
+constexpr int kRangeQueues = 8, kRangeQueueWord = 2;
 
 // Packed sequences up to which the plan orders the chained kernel's work
 // units by their index inside the sequence (above it: sequence by sequence,

@@ -476,7 +476,12 @@ def test_conv_rejects_tensor_on_another_device(name):
 def test_chained_chunks_per_unit(lib, kw, units):
     base = dict(ngroups=1, dstate=128)
     base.update(kw)
-    assert ssd.workspace_layout(P(**base)).chain_chunks_per_unit == units
+    lay = ssd.workspace_layout(P(**base))
+    assert lay.chain_chunks_per_unit == units
+    # balanced ranges only for the 2.7B-shaped batch: 256 CUs (the value
+    # taken without a GPU) hold 512 segment workgroups, one range each
+    want = 512 if kw == dict(batch=8, seqlen=2048, nheads=80) else 0
+    assert lay.chain_ranges == want
 
 
 def test_noalloc_refuses_a_problem_above_its_scratch(lib):

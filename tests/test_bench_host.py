@@ -46,6 +46,13 @@ def test_chain_cost_of_the_2_7b_workload_by_hand():
     two = bench.algorithmic_cost(w, inp, chunks_per_unit=2)
     assert two["ssd_chain"]["overhead_bytes"] == seqs * 3 * H * handoff == 125_829_120
     assert two["ssd_chain"]["bytes"] == want
+    # 512 balanced ranges of the 5,120 (sequence, head, chunk) units, 10 chunks
+    # each, in 8 queues of 64 over 80 pairs each: range t of a queue starts
+    # inside a sequence of 8 chunks unless 10 t % 8 == 0, i.e. for 48 of the
+    # 63 inner starts of each queue, 384 in all
+    rng = bench.algorithmic_cost(w, inp, chunks_per_unit=8, ranges=512)
+    assert rng["ssd_chain"]["overhead_bytes"] == 384 * handoff == 25_165_824
+    assert rng["ssd_chain"]["bytes"] == want
     # masked product 2 tri P, chunk state and C h_in 2 x 2 q N P, state carry 2 P N
     flops = chunks * H * (2 * tri * P + 4 * q * N * P + 2 * P * N)
     assert cost["ssd_chain"]["flops"] == flops
