@@ -293,6 +293,12 @@ __device__ __forceinline__ f32x4 ring_load4(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice));
 }
 
+// Work units (= workgroups) of a one-chunk-unit launch: every (chunk, head)
+// of a dense batch, or every chunk slot of packed input times the heads.
+__host__ __device__ inline int64_t chain_grid(const Args &a) {
+  return (int64_t)(a.varlen ? a.nc_max : a.nseq * a.nc_per) * a.H;
+}
+
 // Per-(chunk, head) state slots in the workspace (the state leaving a chunk,
 // and a chunk's aggregate), in the state-tile layout of the waves (tile (j,
 // pt) of wave w: rows n = 16 (w NTW + j) + 4(lane/16) + r, column p = 16 pt
@@ -458,6 +464,21 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
         if (t < per) got = q * per + t;
       }
       sTicket = got;
+    } else if (!kSeg && !kDeep && a.gqueue) {
+      // one queue per XCD over an eighth of the heads (whole groups), taken
+      // in chunk order: the workgroups sharing an L2 read the same group's
+      // B^T and C B^T tiles, and a unit's predecessor (same head) comes
+      // earlier from the same queue
+      unsigned x;
+      asm volatile("s_getreg_b32 %0, hwreg(20, 0, 4)" : "=s"(x));  // XCC_ID
+      const int per = (int)(chain_grid(a) / kRangeQueues);
+      int got = -1;
+      for (int d = 0; d < kRangeQueues && got < 0; ++d) {
+        const int q = (int)((x + d) % kRangeQueues);
+        const int t = atomicAdd(a.sync + kRangeQueueWord + q, 1);
+        if (t < per) got = q * per + t;
+      }
+      sTicket = got;
     } else {
       sTicket = atomicAdd(ticket, 1);
     }
@@ -474,6 +495,20 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     const int64_t u0 = p0 * a.nc_per, units = (p1 - p0) * a.nc_per;
     rlo = u0 + t * units / per;
     rhi = u0 + (t + 1) * units / per;
+  } else if (!kSeg && !kDeep && a.gqueue) {
+    if (tk < 0) return;  // (every workgroup finds a unit: as many units as workgroups)
+    const int per = (int)(chain_grid(a) / kRangeQueues), q = tk / per, t = tk - q * per;
+    const int hq = a.H / kRangeQueues;
+    if (!a.varlen) {
+      const int j = t / (a.nseq * hq), r = t - j * (a.nseq * hq), s = r / hq;
+      h = q * hq + (r - s * hq);
+      c0 = s * a.nc_per + j;
+    } else {
+      const int kk = t / hq;
+      h = q * hq + (t - kk * hq);
+      if (kk >= a.plan[0]) return;  // unused slot: uniform per workgroup
+      c0 = a.plan[a.order_off + kk];
+    }
   } else if (!a.varlen) {
     const int per = a.nseq * a.H;
     const int j = tk / per, r = tk - j * per, s = r / a.H;
@@ -937,6 +972,13 @@ int64_t chain_units(const Args &a) {
   if (!a.varlen) return (int64_t)a.nseq * ((a.nc_per + s - 1) / s) * a.H;
   // sum over sequences of ceil(chunks / s) <= (chunks + sequences (s - 1)) / s
   return (((int64_t)a.nc_max + (int64_t)a.nseq * (s - 1)) / s) * a.H;
+}
+
+// One-chunk units on large grids take their units from one queue per XCD,
+// each over whole groups, when there are at least 8 groups (with fewer,
+// every XCD would still need every chunk's tiles).
+bool chain_group_queues(const Args &a) {
+  return a.seg <= 1 && !chain_lookback(a) && a.G % kRangeQueues == 0 && a.H % kRangeQueues == 0;
 }
 
 // Whether the launch takes the kDeep kernel, whose units publish aggregates

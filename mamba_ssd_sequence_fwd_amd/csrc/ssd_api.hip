@@ -244,6 +244,7 @@ ssd::Args make_args(const ssd_problem *p, const Layout &L, const void *x, const 
   a.nseg_off = varlen ? 3 + p->num_seqs : 0;
   a.seg = L.path == kMfmaChain ? L.seg : 1;
   a.nrange = L.path == kMfmaChain ? ssd::chain_ranges(a, device_compute_units()) : 0;
+  a.gqueue = L.path == kMfmaChain && ssd::chain_group_queues(a) ? 1 : 0;
   return a;
 }
 

@@ -52,6 +52,8 @@ struct Args {
   int32_t nseg_off;     // int offset inside plan of the number of segments (varlen)
   int32_t nrange;       // chain path, dense input: > 0 when each workgroup takes one of
                         // nrange balanced ranges of the (sequence, head, chunk) order
+  int32_t gqueue;       // chain path, one-chunk units on large grids: 1 when the units
+                        // come from one queue per XCD, each over an eighth of the heads
 };
 
 // Ints ahead of the per-(chunk, head) status words in Args::sync, and the
@@ -218,6 +220,7 @@ bool chain_path_supports(const Args &a);
 hipError_t launch_chain(const Args &a, const void *cb, const void *bt, hipStream_t s);
 int chain_segment(const Args &a);
 int chain_ranges(const Args &a, int compute_units);
+bool chain_group_queues(const Args &a);
 bool chain_lookback(const Args &a);
 bool f32seq_path_supports(const Args &a);
 hipError_t launch_f32seq(const Args &a, hipStream_t s);

@@ -59,6 +59,13 @@ SMALL = {
     "seg-slow-h0": si.scaled(S["S1"], batch=2, seqlen=1800, nheads=52, seed=2031),
     "seg-varlen-slow": si.scaled(S["S3"], nheads=40, num_seqs=9, h0_std=0.1, seed=2032,
                                  seq_lens=(1, 600, 0, 257, 1300, 513, 40, 768, 1025)),
+    # eight or more groups: one-chunk units handed out from one queue per XCD,
+    # each over whole groups (N = 256 dense; packed input at N = 128 with more
+    # units than the chip holds), slow decay so that every carry shows
+    "gqueue-N256-G8": si.scaled(S["S1"], batch=2, seqlen=900, nheads=16, dstate=256, ngroups=8,
+                                seed=2033),
+    "gqueue-varlen-G8": si.scaled(S["S3"], nheads=64, ngroups=8, num_seqs=6, h0_std=0.1,
+                                  seq_lens=(300, 0, 1200, 257, 900, 40), seed=2034),
     "bf16-P32-N48": si.scaled(C[1], batch=1, seqlen=333, nheads=4, headdim=32, dstate=48,
                               chunk=128, seed=2021),
     "bf16-N64": si.scaled(C[2], batch=1, seqlen=520, nheads=4, dstate=64, seed=2022),
