@@ -273,23 +273,23 @@ __device__ __forceinline__ void store_tile(int i, const f32x4 (&Y)[2][4], int le
 }
 
 // The state hand-off between workgroups that may sit on different XCDs
-// (each with its own L2). Ring entries are written and read by 16-byte buffer
+// (each with its own L2). State slots are written and read by 16-byte buffer
 // accesses with the sc1 cache policy (device scope, the same bits a relaxed
 // device-scope atomic access carries), which are coherent across the whole
-// GPU without flushing or invalidating any cache: a producer's ring stores
-// are complete once its s_waitcnt vmcnt(0) returns, it then bumps the
-// counter, and a consumer issues its ring loads only after it has seen the
-// counter. The counter alone orders the hand-off, so the entries need no
+// GPU without flushing or invalidating any cache: a producer's slot stores
+// are complete once its s_waitcnt vmcnt(0) returns, it then sets the chunk's
+// status word, and a consumer issues its slot loads only after it has seen
+// the status. The status alone orders the hand-off, so the slots need no
 // atomicity of their own.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kCachePolicyDevice = 16;  // sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const float *slot, int bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const float *slot, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(slot), (short)0, bytes, 0x00020000);
 }
-__device__ __forceinline__ void ring_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+__device__ __forceinline__ void slot_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kCachePolicyDevice);
 }
-__device__ __forceinline__ f32x4 ring_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ f32x4 slot_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyDevice));
 }
 
@@ -310,11 +310,11 @@ __device__ __forceinline__ uint32_t slot_off(int wave, int ntw, int j, int pt, i
 template <int N, int NTW>
 __device__ __forceinline__ void load_slot(f32x4 (&v)[NTW][4], const float *slot, int wave,
                                           int lane) {
-  const __amdgpu_buffer_rsrc_t r = ring_rsrc(slot, kP * N * 4);
+  const __amdgpu_buffer_rsrc_t r = slot_rsrc(slot, kP * N * 4);
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) v[j][pt] = ring_load4(r, slot_off(wave, NTW, j, pt, lane));
+    for (int pt = 0; pt < 4; ++pt) v[j][pt] = slot_load4(r, slot_off(wave, NTW, j, pt, lane));
 }
 
 // The initial state of head h of sequence s (or zeros), this wave's tiles.
@@ -404,7 +404,7 @@ __device__ __forceinline__ int wait_status(const int32_t *st) {
 // (sequence, head), walked in order by the same workgroup. Inside a segment
 // the state passes from chunk to chunk in registers (it is carried through
 // the output phase of the chunk before), so only the segment's last chunk
-// writes the ring and only its first reads it: a segment of k chunks moves
+// publishes its state and only its first reads one: a segment of k chunks moves
 // 1/k of the hand-off bytes of k one-chunk units. The carried state costs 32
 // registers (N = 128), so segments run two workgroups per CU.
 //
@@ -718,11 +718,11 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
                                  __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (sReady != kIncReady) {
-      const __amdgpu_buffer_rsrc_t r = ring_rsrc(a.agg + ((size_t)c * a.H + h) * PN, (int)(PN * 4));
+      const __amdgpu_buffer_rsrc_t r = slot_rsrc(a.agg + ((size_t)c * a.H + h) * PN, (int)(PN * 4));
 #pragma unroll
       for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) ring_store4(r, slot_off(wave, NTW, j, pt, lane), hs[j][pt]);
+        for (int pt = 0; pt < 4; ++pt) slot_store4(r, slot_off(wave, NTW, j, pt, lane), hs[j][pt]);
       if (tid == 0)
         __hip_atomic_store(decw + (size_t)c * a.H + h, __float_as_int(cs_last), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -796,12 +796,12 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
       for (int pt = 0; pt < 4; ++pt) hcarry[j][pt] = step_state(dec, hin[j][pt], hs[j][pt]);
   } else if (!last) {
     const __amdgpu_buffer_rsrc_t rout =
-        ring_rsrc(inc_slot<N, kDeep>(a, c, k.idx, k.seq, h), (int)(PN * 4));
+        slot_rsrc(inc_slot<N, kDeep>(a, c, k.idx, k.seq, h), (int)(PN * 4));
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-        ring_store4(rout, slot_off(wave, NTW, j, pt, lane), step_state(dec, hin[j][pt], hs[j][pt]));
+        slot_store4(rout, slot_off(wave, NTW, j, pt, lane), step_state(dec, hin[j][pt], hs[j][pt]));
   } else if (a.hT) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
