@@ -200,108 +200,6 @@ __device__ __forceinline__ void intra_tile(int i, f32x4 (&Y)[2][4], CbStream &st
     diag(st.a);
 }
 
-// The same products with the C B^T tiles loaded inside, one stream of two
-// buffers rotated by copies (so each step waits for the next one's tiles as
-// well), in a loop: what the segment kernel keeps, where the unrolled
-// stream's code (about three times the size) measured no faster (the 2.7B
-// shapes: 156.3 against 153.9 us per pass, order-balanced A/B).
-//
-// Intra-chunk outputs of the 32-row tile i (rows 32i .. 32i+31), both 16-row
-// halves u, added into Y[u] (transposed: lane holds column l = 32i + 16u +
-// lane%16 and rows p = 16pt + 4(lane/16) + r). Off-diagonal 32-token tiles
-// j < i use the split decay 2^(cs_l - cs_r0) 2^(cs_r0 - cs_e) 2^(cs_e - cs_s)
-// (three factors <= 1, e = last token of tile j, r0 = first row of tile i,
-// the last one folded into sU); the diagonal tile takes the exact masked
-// exponent and carries D on its diagonal. C B^T tiles stream from L2 two
-// ahead; each x operand read serves both halves.
-template <int Q>
-__device__ __forceinline__ void intra_tile_rolled(int i, f32x4 (&Y)[2][4], const bf16 *sX,
-                                           const float *sCs, const float *sDt, const float *sU,
-                                           const bf16 *cbase, float dsk, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-  const int pair0 = i * (i + 1) / 2;
-  const float cs_r0 = sCs[32 * i];
-  float cs_l[2], rdec[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    cs_l[u] = sCs[32 * i + 16 * u + lr];
-    rdec[u] = exp2_fast(cs_l[u] - cs_r0);
-  }
-  const int xrow = 4 * lg + (lr >> 2);
-  int xoff[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) xoff[pt] = xrow * kP + tr_lane_off<kP>(16 * pt, xrow & 7);
-
-  bf16x8 m0[2], m1[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    m0[u] = ldg8(cbase + (size_t)(pair0 * 2 + u) * 512);
-    m1[u] = ldg8(cbase + (size_t)((pair0 + min(1, i)) * 2 + u) * 512);
-  }
-#pragma unroll 1
-  for (int j = 0; j < i; ++j) {
-    bf16x8 m[2] = {m0[0], m0[1]};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      m0[u] = m1[u];
-      m1[u] = ldg8(cbase + (size_t)((pair0 + min(j + 2, i)) * 2 + u) * 512);
-    }
-    // LDS reads first (they return in order): the decay inputs, then every
-    // x operand of the step, whose latency the scaling below then hides.
-    const float cs_e = sCs[32 * j + 31];
-    const float4 ua = *reinterpret_cast<const float4 *>(sU + 32 * j + 4 * lg);
-    const float4 ub = *reinterpret_cast<const float4 *>(sU + 32 * j + 16 + 4 * lg);
-    bf16x8 xv[4];
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const bf16x4 lo = ds_tr4(sX, 32 * j * kP + xoff[pt]);
-      const bf16x4 hi = ds_tr4(sX, (32 * j + 16) * kP + xoff[pt]);
-      xv[pt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    const float e_r0 = exp2_fast(cs_r0 - cs_e);
-    const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float fa = rdec[u] * e_r0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m[u][e] = (bf16)((float)m[u][e] * (fa * uu[e]));
-    }
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(xv[pt], m[u], Y[u][pt]);
-  }
-  // Diagonal tile j = i (m0 holds it: the stream clamps at i).
-  {
-    const float4 ca = *reinterpret_cast<const float4 *>(sCs + 32 * i + 4 * lg);
-    const float4 cb4 = *reinterpret_cast<const float4 *>(sCs + 32 * i + 16 + 4 * lg);
-    const float4 da = *reinterpret_cast<const float4 *>(sDt + 32 * i + 4 * lg);
-    const float4 db = *reinterpret_cast<const float4 *>(sDt + 32 * i + 16 + 4 * lg);
-    const float cc[8] = {ca.x, ca.y, ca.z, ca.w, cb4.x, cb4.y, cb4.z, cb4.w};
-    const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-    bf16x8 m[2] = {m0[0], m0[1]};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int lloc = 16 * u + lr;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sloc = 16 * (e >> 2) + 4 * lg + (e & 3);
-        const float v = (float)m[u][e] * exp2_fast(cs_l[u] - cc[e]) * dd[e];
-        const float w = sloc == lloc ? v + dsk : v;
-        m[u][e] = (bf16)(sloc <= lloc ? w : 0.f);
-      }
-    }
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const bf16x4 lo = ds_tr4(sX, 32 * i * kP + xoff[pt]);
-      const bf16x4 hi = ds_tr4(sX, (32 * i + 16) * kP + xoff[pt]);
-      const bf16x8 xv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) Y[u][pt] = mfma(xv, m[u], Y[u][pt]);
-    }
-  }
-}
-
 // C rows of the 32-row tile i, both halves: row 32i + 16u + lane%16 (clamped
 // into the chunk), n = 32ks + 8(lane/16) .. +7.
 template <int N>
@@ -674,11 +572,6 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     dtb = a.dt_softplus && a.dt_bias ? a.dt_bias[h] : 0.f;
   };
   f32x4 hcarry[NTW][4];  // kSeg: the state leaving the previous chunk of the segment
-  // kSeg, dense input: dt and x of the segment's next chunk, loaded by the
-  // chunk before it ahead of its last y stores (a load issued after those
-  // stores could only be waited for together with them)
-  bf16 dt_next;
-  bf16x8 x_next[NKS];
   // x rows of one chunk into registers, one instruction per 32-token step
   // (instruction k of wave w: rows 32k + 8w + lane/8, 16 bytes each; rows
   // past len repeat the last row)
@@ -715,9 +608,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   // 32-token step (instruction k of wave w: rows 32k + 8w + lane/8, 16 bytes
   // each). x reaches LDS step by step, so S_c starts once the first half has
   // arrived.
-  const bool prefetched = kSeg && !a.varlen && ci > 0;
-  const bf16 dtraw = prefetched ? dt_next
-                                : static_cast<const bf16 *>(a.dt)[(size_t)(k.start + min(tid, k.len - 1)) * a.H + h];
+  const bf16 dtraw = static_cast<const bf16 *>(a.dt)[(size_t)(k.start + min(tid, k.len - 1)) * a.H + h];
   const int pair = k.seq * a.H + h;
   const bool first = k.idx == 0;
   int early = 0;  // the predecessor's status, read early
@@ -736,12 +627,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     for (int ks = 0; ks < KPF; ++ks) bts[j][ks] = ldg8(btc + (size_t)(j * NKS + ks) * 512);
   const int xrl = lane >> 3, xcol = lane & 7;
   bf16x8 xr[NKS];
-  if (prefetched) {
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) xr[ks] = x_next[ks];
-  } else {
-    load_x(xc, k.len, lane, xr);
-  }
+  load_x(xc, k.len, lane, xr);
   float dtv = (float)dtraw;
   if (a.dt_softplus) dtv = softplus_f32(dtv + dtb);
   dtv = tid < k.len ? dtv : 0.f;  // zero past the chunk end (and for tid >= Q)
@@ -967,45 +853,25 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   if (tail) load_c_tile<N>(acA, cc, ldb, iA, k.len, lane);
 
   // ---- 4. outputs, one 32-row tile at a time ------------------------------------
-  // dt and x of the segment's next chunk (same sequence: a dense segment
-  // never crosses one), issued after the last C B^T tile loads of this chunk
-  // and before its last y stores
-  auto prefetch_next = [&]() {
-    if (kSeg && !a.varlen && ci + 1 < nk) {
-      const int nstart = k.start + Q, nlen = min(Q, a.L - (k.idx + 1) * Q);
-      dt_next = static_cast<const bf16 *>(a.dt)[(size_t)(nstart + min(tid, nlen - 1)) * a.H + h];
-      load_x(static_cast<const bf16 *>(a.x) + (size_t)nstart * ldx + (size_t)h * kP, nlen, lane,
-             x_next);
-    }
-  };
   const bf16 *cbase = cb + ((size_t)c * a.G + g) * PAIRS * 2 * 512 + lane * 8;
   bf16 *yc = static_cast<bf16 *>(a.y) + (size_t)k.start * ldx + (size_t)h * kP;
   bf16x8 acB[2][N / 32];
   CbStream sA, sB;
   {
     f32x4 Y[2][4];
-    if (!kSeg) cb_begin(iA, sA, cbase);  // in flight during the state product
+    cb_begin(iA, sA, cbase);  // in flight during the state product
     state_tile<N>(iA, Y, sH, sCs, acA, k.len, lane);
-    if (kSeg)
-      intra_tile_rolled<Q>(iA, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
-    else
-      intra_tile<Q>(iA, Y, sA, sX, sCs, sDt, sU, cbase, dsk, lane);
+    intra_tile<Q>(iA, Y, sA, sX, sCs, sDt, sU, cbase, dsk, lane);
     if (NTILE == 2) {  // the second tile's first loads, in flight during the stores
       load_c_tile<N>(acB, cc, ldb, iB, k.len, lane);
-      if (!kSeg) cb_begin(iB, sB, cbase);
-    } else {
-      prefetch_next();
+      cb_begin(iB, sB, cbase);
     }
     store_tile(iA, Y, k.len, yc, ldx, lane);
   }
   if (NTILE == 2) {
     f32x4 Y[2][4];
     state_tile<N>(iB, Y, sH, sCs, acB, k.len, lane);
-    if (kSeg)
-      intra_tile_rolled<Q>(iB, Y, sX, sCs, sDt, sU, cbase, dsk, lane);
-    else
-      intra_tile<Q>(iB, Y, sB, sX, sCs, sDt, sU, cbase, dsk, lane);
-    prefetch_next();
+    intra_tile<Q>(iB, Y, sB, sX, sCs, sDt, sU, cbase, dsk, lane);
     store_tile(iB, Y, k.len, yc, ldx, lane);
   }
   return true;
