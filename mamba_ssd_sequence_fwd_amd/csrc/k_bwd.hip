@@ -32,9 +32,9 @@
 
 namespace ssd {
 
-// dB / dC kernel: 8 waves per workgroup (more loads in flight per CU while
-// each head's operands are staged).
-constexpr int kDbcThreads = 512;
+// dB / dC kernel: 16 waves per workgroup at N = 128 (128 VGPRs each, one
+// workgroup per CU), 8 at N = 64.
+template <int N> constexpr int dbc_threads() { return N == 128 ? 1024 : 512; }
 
 bool bwd_supports(const Args &a) {
   return a.P == kP && (a.N == 64 || a.N == 128) && (a.Q == 128 || a.Q == 256);
@@ -494,9 +494,9 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 }
 
 // ---------------------------------------------------------------------------
-// dB and dC: one workgroup (8 waves) per (chunk, group, block of kBwdRows
-// tokens r0 .. r0 + 31), summing over the heads of the group. Per head it
-// adds, into fp32 accumulators:
+// dB and dC: one workgroup per (chunk, group, block of kBwdRows tokens
+// r0 .. r0 + 31), summing over the heads of the group. Per head it adds,
+// into fp32 accumulators:
 //   ZR[s][l] = Z_h[l, s] for l in the block and s <= l       (feeds dC rows l)
 //   ZC[l][s] = Z_h[l, s] for s in the block and l >= s       (feeds dB rows s)
 //   DC[n][l] += sum_p h_in[p][n] 2^(cs_l) dy[l][p]           (dC state term)
@@ -505,14 +505,19 @@ __global__ __launch_bounds__(256) void k_bwd_dx(BwdArgs b) {
 // each Z tile computed as x . dy^T or dy . x^T over p. Z's 16 x 16 tiles are
 // taken in pairs (a 32-token K step of the final products); the 2 + 2 Q/32
 // pairs, and the (n tile, half) tiles of DC and DB, are dealt round-robin to
-// the 8 waves. After the last head the pairs go
-// to LDS as bf16 column operands in the token order of the transposed B / C
-// reads, and DC += B^T-ZR, DB += C^T-ZC finish the sums. Workgroups of one
-// chunk run on one XCD so the per-head operands they all read share an L2.
+// the waves. The decay factor of an off-diagonal Z element is a column
+// factor times a row factor (split at the block's ends, both <= 1); the
+// state terms are scaled after each head's product. The head's operands go
+// through two LDS buffers (head j + 1 is written while head j is read, one
+// barrier per head). After the last head the pairs go to LDS as bf16 column
+// operands in the token order of the transposed B / C reads, and DC +=
+// B^T-ZR, DB += C^T-ZC finish the sums. Workgroups of one chunk run on one
+// XCD so the per-head operands they all read share an L2.
 // ---------------------------------------------------------------------------
 template <int N, int Q>
-__global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
+__global__ __launch_bounds__(dbc_threads<N>()) void k_bwd_dbc(BwdArgs b) {
   const Args &a = b.f;
+  constexpr int kDbcThreads = dbc_threads<N>();
   constexpr int NW = kDbcThreads / 64;  // waves
   constexpr int R = kBwdRows;
   constexpr int NB = Q / R;
@@ -524,10 +529,9 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
   // One LDS area: the per-head operands during the head loop, then the B / C
   // rows and the Z operands (small enough for two workgroups per CU).
   constexpr int kLoop = XROWS * kP + 2 * N * kP, kFinal = BROWS * N + NPAIR * 512;
-  __shared__ __attribute__((aligned(16))) bf16 sMem[kLoop > kFinal ? kLoop : kFinal];
-  bf16 *const sXD = sMem, *const sHt = sMem + XROWS * kP, *const sGt = sHt + N * kP;
+  __shared__ __attribute__((aligned(16))) bf16 sMem[2 * kLoop > kFinal ? 2 * kLoop : kFinal];
   bf16 *const sBC = sMem, *const sZ = sMem + BROWS * N;
-  __shared__ __attribute__((aligned(16))) float sCs[Q], sDt[Q];
+  __shared__ __attribute__((aligned(16))) float sTab[2][3][Q];
 
   const int nb = gridDim.x, bid = blockIdx.x;
   const int q8 = nb >> 3, r8 = nb & 7, xcd = bid & 7;
@@ -557,69 +561,84 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
   // store, so the compiler has no reason to wait for them early. Rows past
   // the chunk end hold copies of its last row: every product that reads
   // them is masked (l < len) or scaled by zero.
-  constexpr int XI = (XROWS * (kP / 8) + kDbcThreads - 1) / kDbcThreads;
-  constexpr int HI = (N * (kP / 8) + kDbcThreads - 1) / kDbcThreads;
-  constexpr int TI = (Q + kDbcThreads - 1) / kDbcThreads;
-  bf16x8 vx[XI], vh[HI], vg[HI];
-  float vcs[TI];
-  bf16 vdt[TI];
+  // Each load instruction is issued only by the waves that need it (the
+  // vector memory pipe, not the bandwidth, bounds the head walk): XF full
+  // rounds of 16-byte x / dy pieces, a last partial round of XR pieces by the
+  // first XR threads, the bf16 states (one piece per thread), and the decays
+  // and steps of the chunk by threads XR .. XR + Q.
+  constexpr int XU = XROWS * (kP / 8), XF = XU / kDbcThreads, XR = XU % kDbcThreads;
+  static_assert(XR % 64 == 0 && XR + Q <= kDbcThreads, "wave-uniform load split");
+  static_assert(N * (kP / 8) == kDbcThreads, "one state piece per thread");
+  bf16x8 vx[XF + 1], vh, vg;
+  float vcs, vref[3];
+  bf16 vdt;
   auto fetch = [&](int h) {
     const bf16 *xs = static_cast<const bf16 *>(a.x) + ((size_t)k.start * a.H + h) * kP;
     const bf16 *dys = static_cast<const bf16 *>(b.dy) + ((size_t)k.start * a.H + h) * kP;
     const bf16 *hinT = b.hinT + ((size_t)c * a.H + h) * N * kP;
     const bf16 *gT = b.gT + ((size_t)c * a.H + h) * N * kP;
 #pragma unroll
-    for (int i = 0; i < XI; ++i) {
-      const int it = min(tid + i * kDbcThreads, XROWS * (kP / 8) - 1);
+    for (int i = 0; i <= XF; ++i) {
+      if (i == XF && tid >= XR) break;  // wave-uniform
+      const int it = tid + i * kDbcThreads;
       const int row = it / (kP / 8), col = (it % (kP / 8)) * 8;
       const bf16 *src = row < nxr ? xs + (size_t)min(row, len - 1) * ldx
                                   : dys + (size_t)min(row - R, len - 1) * ldx;
       vx[i] = ldg8(src + col);
     }
-#pragma unroll
-    for (int i = 0; i < HI; ++i) {
-      const int it = min(tid + i * kDbcThreads, N * (kP / 8) - 1);
-      const int n = it / (kP / 8), p0 = (it % (kP / 8)) * 8;
-      vh[i] = ldg8(hinT + (size_t)n * kP + p0);
-      vg[i] = ldg8(gT + (size_t)n * kP + p0);
-    }
+    vh = ldg8(hinT + (size_t)(tid / (kP / 8)) * kP + (tid % (kP / 8)) * 8);
+    vg = ldg8(gT + (size_t)(tid / (kP / 8)) * kP + (tid % (kP / 8)) * 8);
     const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
+    if (tid >= XR && tid < XR + Q) {  // wave-uniform
+      const int t = min(tid - XR, len - 1);
+      vcs = cs[t];
+      vdt = static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
+    }
+    vref[0] = cs[r0];                      // the block's first token
+    vref[1] = cs[min(r0 + R, len) - 1];    // its last (inside the chunk)
+    vref[2] = cs[len - 1];                 // the chunk's last
+  };
+  // writes the fetched head into LDS buffer `buf`
+  auto stage = [&](int buf) {
+    bf16 *const sXD = sMem + buf * kLoop, *const sHt = sXD + XROWS * kP, *const sGt = sHt + N * kP;
+    float *const sCs = sTab[buf][0], *const sDt = sTab[buf][1], *const sW = sTab[buf][2];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int t = min(min(tid + i * kDbcThreads, Q - 1), len - 1);
-      vcs[i] = cs[t];
-      vdt[i] = static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
+    for (int i = 0; i <= XF; ++i) {
+      if (i == XF && tid >= XR) break;
+      const int it = tid + i * kDbcThreads;
+      *reinterpret_cast<bf16x8 *>(sXD + rswz<kP>(it / (kP / 8), (it % (kP / 8)) * 8)) = vx[i];
+    }
+    *reinterpret_cast<bf16x8 *>(sHt + rswz<kP>(tid / (kP / 8), (tid % (kP / 8)) * 8)) = vh;
+    *reinterpret_cast<bf16x8 *>(sGt + rswz<kP>(tid / (kP / 8), (tid % (kP / 8)) * 8)) = vg;
+    // Decay factors of the head, split at the block's ends so that no factor
+    // exceeds 1: W[t] = dt_t 2^(cs_r0 - cs_t) before the block, 2^(cs_t -
+    // cs_e) after it (e its last token), 0 inside it and past the chunk end.
+    const float cs_r0 = vref[0], cs_e = vref[1];
+    if (tid >= XR && tid < XR + Q) {
+      const int t = tid - XR;
+      const float dtv = t < len ? (float)vdt : 0.f;
+      sCs[t] = vcs;
+      sDt[t] = dtv;
+      sW[t] = t < r0 ? dtv * exp2_fast(cs_r0 - vcs)
+                     : (t >= r0 + R && t < len ? exp2_fast(vcs - cs_e) : 0.f);
     }
   };
+  // Two LDS buffers: head j is read from buffer j % 2 while head j + 1,
+  // loaded into registers meanwhile, is written into the other; one barrier
+  // per head.
   fetch(g * a.heads_per_group);
+  stage(0);
+  __syncthreads();
   for (int hj = 0; hj < a.heads_per_group; ++hj) {
-    __syncthreads();  // the previous head's operands are consumed
-#pragma unroll
-    for (int i = 0; i < XI; ++i) {
-      const int it = tid + i * kDbcThreads;
-      if (it < XROWS * (kP / 8))
-        *reinterpret_cast<bf16x8 *>(sXD + rswz<kP>(it / (kP / 8), (it % (kP / 8)) * 8)) = vx[i];
-    }
-#pragma unroll
-    for (int i = 0; i < HI; ++i) {
-      const int it = tid + i * kDbcThreads;
-      if (it < N * (kP / 8)) {
-        const int n = it / (kP / 8), p0 = (it % (kP / 8)) * 8;
-        *reinterpret_cast<bf16x8 *>(sHt + rswz<kP>(n, p0)) = vh[i];
-        *reinterpret_cast<bf16x8 *>(sGt + rswz<kP>(n, p0)) = vg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int t = tid + i * kDbcThreads;
-      if (t < Q) {
-        sCs[t] = vcs[i];
-        sDt[t] = t < len ? (float)vdt[i] : 0.f;
-      }
-    }
-    __syncthreads();
-    if (hj + 1 < a.heads_per_group) fetch(g * a.heads_per_group + hj + 1);
-    const float cs_last = sCs[len - 1];
+    const int buf = hj & 1;
+    const bf16 *const sXD = sMem + buf * kLoop, *const sHt = sXD + XROWS * kP, *const sGt = sHt + N * kP;
+    const float *const sCs = sTab[buf][0], *const sDt = sTab[buf][1], *const sW = sTab[buf][2];
+    const float cs_r0 = vref[0], cs_e = vref[1], cs_last = vref[2];
+    // The next head's loads and staging are unconditional (the last head
+    // fetches itself again, into the unused buffer): a skipped fetch on the
+    // last head would make the compiler assume loads pending at the loop top
+    // and wait for this head's first loads there.
+    fetch(g * a.heads_per_group + min(hj + 1, a.heads_per_group - 1));
 
     // Z pairs of this wave
 #pragma unroll
@@ -632,6 +651,9 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
       // the column token of this pair's tiles (l for ZR, s for ZC)
       const int coltok = r0 + 16 * half + lr;
       const float cs_c = sCs[coltok], dt_c = sDt[coltok];
+      // the column's share of the off-diagonal factor (zr: 2^(cs_l - cs_r0);
+      // zc: dt_s 2^(cs_e - cs_s))
+      const float colf = kb == rb ? 0.f : zr ? exp2_fast(cs_c - cs_r0) : dt_c * exp2_fast(cs_e - cs_c);
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti) {
         const int t16 = 2 * kb + ti;   // the 16-token tile along K of the final product
@@ -646,50 +668,58 @@ __global__ __launch_bounds__(kDbcThreads) void k_bwd_dbc(BwdArgs b) {
           const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(sXD + rswz<kP>(brow, 32 * kp + 8 * lg));
           d = mfma(av, bv, d);
         }
-        // the decay and step of this lane's four row tokens in two 16-byte reads
-        const float4 cs4 = *reinterpret_cast<const float4 *>(sCs + 16 * t16 + 4 * lg);
-        const float4 dt4 = *reinterpret_cast<const float4 *>(sDt + 16 * t16 + 4 * lg);
-        const float csr[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, dtr[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+        if (kb != rb) {
+          // off the block's diagonal: the factor is the column's times W of the row
+          const float4 w4 = *reinterpret_cast<const float4 *>(sW + 16 * t16 + 4 * lg);
+          const float wr[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rowtok = 16 * t16 + 4 * lg + r;
-          const int s = zr ? rowtok : coltok, l = zr ? coltok : rowtok;
-          const bool in = s <= l && l < len;
-          // Z[l, s] = 2^(cs_l - cs_s) dt_s (dy_l . x_s)
-          const float f = zr ? exp2_fast(cs_c - csr[r]) * dtr[r] : exp2_fast(csr[r] - cs_c) * dt_c;
-          zacc[i][ti][r] += in ? d[r] * f : 0.f;
+          for (int r = 0; r < 4; ++r) zacc[i][ti][r] += d[r] * (colf * wr[r]);
+        } else {
+          // the decay and step of this lane's four row tokens in two 16-byte reads
+          const float4 cs4 = *reinterpret_cast<const float4 *>(sCs + 16 * t16 + 4 * lg);
+          const float4 dt4 = *reinterpret_cast<const float4 *>(sDt + 16 * t16 + 4 * lg);
+          const float csr[4] = {cs4.x, cs4.y, cs4.z, cs4.w}, dtr[4] = {dt4.x, dt4.y, dt4.z, dt4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rowtok = 16 * t16 + 4 * lg + r;
+            const int s = zr ? rowtok : coltok, l = zr ? coltok : rowtok;
+            const bool in = s <= l && l < len;
+            // Z[l, s] = 2^(cs_l - cs_s) dt_s (dy_l . x_s)
+            const float f = zr ? exp2_fast(cs_c - csr[r]) * dtr[r] : exp2_fast(csr[r] - cs_c) * dt_c;
+            zacc[i][ti][r] += in ? d[r] * f : 0.f;
+          }
         }
       }
     }
     // state terms of this wave's units (n tile, half): DC[n][l], l = r0 + 16 half + lr,
-    // and DB[n][s], s = r0 + 16 half + lr
+    // and DB[n][s], s = r0 + 16 half + lr; the column scale is applied to the
+    // head's product (one scalar per lane)
 #pragma unroll
     for (int ui = 0; ui < UPW; ++ui) {
       const int u = wave + NW * ui, nt = u >> 1, half = u & 1;
       const int tok = r0 + 16 * half + lr;
-      const float el = tok < len ? exp2_fast(sCs[tok]) : 0.f;
-      const float es = tok < len ? sDt[tok] * exp2_fast(cs_last - sCs[tok]) : 0.f;
       const int n = 16 * nt + lr;
+      f32x4 tc = f32x4{0.f, 0.f, 0.f, 0.f}, tb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kp = 0; kp < kP / 32; ++kp) {
         const bf16x8 dyv = *reinterpret_cast<const bf16x8 *>(sXD + rswz<kP>(R + tok, 32 * kp + 8 * lg));
         const bf16x8 xv = *reinterpret_cast<const bf16x8 *>(sXD + rswz<kP>(tok, 32 * kp + 8 * lg));
-        bf16x8 dyb, xb;
+        tc = mfma(*reinterpret_cast<const bf16x8 *>(sHt + rswz<kP>(n, 32 * kp + 8 * lg)), dyv, tc);
+        tb = mfma(*reinterpret_cast<const bf16x8 *>(sGt + rswz<kP>(n, 32 * kp + 8 * lg)), xv, tb);
+      }
+      const float cs_t = sCs[tok];
+      const float el = tok < len ? exp2_fast(cs_t) : 0.f, es = sDt[tok] * exp2_fast(cs_last - cs_t);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dyb[e] = (bf16)((float)dyv[e] * el);
-          xb[e] = (bf16)((float)xv[e] * es);
-        }
-        dcacc[ui] = mfma(*reinterpret_cast<const bf16x8 *>(sHt + rswz<kP>(n, 32 * kp + 8 * lg)),
-                         dyb, dcacc[ui]);
-        dbacc[ui] = mfma(*reinterpret_cast<const bf16x8 *>(sGt + rswz<kP>(n, 32 * kp + 8 * lg)),
-                         xb, dbacc[ui]);
+      for (int r = 0; r < 4; ++r) {
+        dcacc[ui][r] += el * tc[r];
+        dbacc[ui][r] += es * tb[r];
       }
     }
+    stage(buf ^ 1);
+    __syncthreads();  // head j + 1 is in LDS, and every wave is done with head j
   }
 
   // Z pairs to LDS as column operands (the head loop's operands are dead).
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < PPW; ++i) {
     const int q = wave + NW * i;
@@ -817,7 +847,7 @@ hipError_t launch_bwd_dx(const BwdArgs &b, hipStream_t st) {
 template <int N, int Q>
 static hipError_t launch_dbc_nq(const BwdArgs &b, hipStream_t st) {
   const int64_t blocks = (int64_t)b.f.nc_max * b.f.G * (Q / kBwdRows);
-  hipLaunchKernelGGL((k_bwd_dbc<N, Q>), dim3((unsigned)blocks), dim3(kDbcThreads), 0, st, b);
+  hipLaunchKernelGGL((k_bwd_dbc<N, Q>), dim3((unsigned)blocks), dim3(dbc_threads<N>()), 0, st, b);
   return hipGetLastError();
 }
 
