@@ -904,7 +904,8 @@ ssd_status ssd_backward_timed(const ssd_problem *p, const void *x, const void *d
                               workspace_bytes, &b);
   if (st != SSD_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int kMax = 10;  // stages of enqueue_bwd
+  constexpr int kMax = (int)(sizeof(kBwdStages) / sizeof(kBwdStages[0]));  // stages of enqueue_bwd
+  static_assert(kMax <= SSD_MAX_STAGES, "ssd_stage_times holds every backward stage");
   std::vector<hipEvent_t> ev((size_t)iterations * (kMax + 1), nullptr);
   for (auto &e : ev)
     if (hipEventCreate(&e) != hipSuccess) {
