@@ -120,7 +120,7 @@ TRAFFIC_PROFILES = {
                                        ("k_step.hip", "step.h", "ssd_internal.h")),
     ("ssd_conv", "conv-front-2.7b"): ("ssd_conv_front-2.7b.md",
                                       ("k_conv.hip", "conv.h", "ssd_internal.h")),
-    ("bwd_dbc", "bwd-2.7b-bf16"): ("ssd_backward_2.7b-bf16.md",
+    ("bwd_dx", "bwd-2.7b-bf16"): ("ssd_backward_2.7b-bf16.md",
                                    ("k_bwd.hip", "bwd.h", "mfma_common.h", "ssd_internal.h")),
 }
 
