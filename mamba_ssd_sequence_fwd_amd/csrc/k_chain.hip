@@ -720,13 +720,16 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
 
   // ---- 3. h_in; h_out = 2^(cs_last) h_in + S_c published; ----------------------
   const int iA = wave, iB = T - 1 - wave;
-  if (!ready && !kDeep) {
+  if (!ready && (!kDeep || k.idx == 1)) {
     // The state leaving the previous chunk was not published before S_c:
-    // wait for it (these units publish nothing else).
+    // wait for it (these units publish nothing else). Under kDeep this is
+    // the second chunk of a sequence, whose predecessor (the first chunk)
+    // never waits: it publishes soon, and an aggregate would only delay this
+    // unit.
     if (tid == 0 && wait_status(stat + (size_t)(c - 1) * a.H + h) != kIncReady)
       __hip_atomic_fetch_or(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    load_h_in<N, NTW, false>(hin, a, k, c, h, wave, nt0, lane);
+    load_h_in<N, NTW, kDeep>(hin, a, k, c, h, wave, nt0, lane);
   } else if (!ready) {
     // kDeep (every unit resident at once): rather than wait for the
     // predecessor's own wait, publish this chunk's aggregate (S_c and its
