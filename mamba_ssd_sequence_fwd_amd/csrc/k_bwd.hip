@@ -564,8 +564,9 @@ __global__ __launch_bounds__(dbc_threads<N>()) void k_bwd_dbc(BwdArgs b) {
   // Each load instruction is issued only by the waves that need it (the
   // vector memory pipe, not the bandwidth, bounds the head walk): XF full
   // rounds of 16-byte x / dy pieces, a last partial round of XR pieces by the
-  // first XR threads, the bf16 states (one piece per thread), and the decays
-  // and steps of the chunk by threads XR .. XR + Q.
+  // last XR threads, the bf16 states (one piece per thread), and the decays
+  // and steps of the chunk by the Q threads before those (the last waves,
+  // whose Z pairs are the fewer).
   constexpr int XU = XROWS * (kP / 8), XF = XU / kDbcThreads, XR = XU % kDbcThreads;
   static_assert(XR % 64 == 0 && XR + Q <= kDbcThreads, "wave-uniform load split");
   static_assert(N * (kP / 8) == kDbcThreads, "one state piece per thread");
@@ -579,8 +580,8 @@ __global__ __launch_bounds__(dbc_threads<N>()) void k_bwd_dbc(BwdArgs b) {
     const bf16 *gT = b.gT + ((size_t)c * a.H + h) * N * kP;
 #pragma unroll
     for (int i = 0; i <= XF; ++i) {
-      if (i == XF && tid >= XR) break;  // wave-uniform
-      const int it = tid + i * kDbcThreads;
+      if (i == XF && tid < kDbcThreads - XR) break;  // wave-uniform
+      const int it = i == XF ? tid - (kDbcThreads - XR) + i * kDbcThreads : tid + i * kDbcThreads;
       const int row = it / (kP / 8), col = (it % (kP / 8)) * 8;
       const bf16 *src = row < nxr ? xs + (size_t)min(row, len - 1) * ldx
                                   : dys + (size_t)min(row - R, len - 1) * ldx;
@@ -589,8 +590,8 @@ __global__ __launch_bounds__(dbc_threads<N>()) void k_bwd_dbc(BwdArgs b) {
     vh = ldg8(hinT + (size_t)(tid / (kP / 8)) * kP + (tid % (kP / 8)) * 8);
     vg = ldg8(gT + (size_t)(tid / (kP / 8)) * kP + (tid % (kP / 8)) * 8);
     const float *cs = a.cs + ((size_t)c * a.H + h) * Q;
-    if (tid >= XR && tid < XR + Q) {  // wave-uniform
-      const int t = min(tid - XR, len - 1);
+    if (tid >= kDbcThreads - XR - Q && tid < kDbcThreads - XR) {  // wave-uniform
+      const int t = min(tid - (kDbcThreads - XR - Q), len - 1);
       vcs = cs[t];
       vdt = static_cast<const bf16 *>(a.dt)[(size_t)(k.start + t) * a.H + h];
     }
@@ -604,8 +605,8 @@ __global__ __launch_bounds__(dbc_threads<N>()) void k_bwd_dbc(BwdArgs b) {
     float *const sCs = sTab[buf][0], *const sDt = sTab[buf][1], *const sW = sTab[buf][2];
 #pragma unroll
     for (int i = 0; i <= XF; ++i) {
-      if (i == XF && tid >= XR) break;
-      const int it = tid + i * kDbcThreads;
+      if (i == XF && tid < kDbcThreads - XR) break;
+      const int it = i == XF ? tid - (kDbcThreads - XR) + i * kDbcThreads : tid + i * kDbcThreads;
       *reinterpret_cast<bf16x8 *>(sXD + rswz<kP>(it / (kP / 8), (it % (kP / 8)) * 8)) = vx[i];
     }
     *reinterpret_cast<bf16x8 *>(sHt + rswz<kP>(tid / (kP / 8), (tid % (kP / 8)) * 8)) = vh;
@@ -614,8 +615,8 @@ __global__ __launch_bounds__(dbc_threads<N>()) void k_bwd_dbc(BwdArgs b) {
     // exceeds 1: W[t] = dt_t 2^(cs_r0 - cs_t) before the block, 2^(cs_t -
     // cs_e) after it (e its last token), 0 inside it and past the chunk end.
     const float cs_r0 = vref[0], cs_e = vref[1];
-    if (tid >= XR && tid < XR + Q) {
-      const int t = tid - XR;
+    if (tid >= kDbcThreads - XR - Q && tid < kDbcThreads - XR) {
+      const int t = tid - (kDbcThreads - XR - Q);
       const float dtv = t < len ? (float)vdt : 0.f;
       sCs[t] = vcs;
       sDt[t] = dtv;
