@@ -950,18 +950,28 @@ constexpr int64_t kDeepMaxUnits = 3 * 256;
 // once. Order-balanced A/B on one box, with whole-row y stores, the 2.7B-shaped
 // workload: units of 1, 2, 3 and 4 chunks within 3% of each other (163-170 us
 // per pass over two rounds), so the longest is taken: it moves the fewest
-// hand-off bytes (42 MB per launch against 294 MB for one-chunk units). The
-// long packed workload lost with segments (1586 -> 1631 us with units of 2),
-// being the more sensitive to the third workgroup per CU that segments give
-// up, so packed input keeps one-chunk units.
+// hand-off bytes (42 MB per launch against 294 MB for one-chunk units).
 constexpr int kChainSeg = 4;
 
+// Packed input: segments of up to 12 chunks when there are at least twice as
+// many (sequence, head) pairs as the chip holds segment workgroups (2 per CU
+// on 256 CUs), so that one pair's walk, chunk after chunk inside a workgroup,
+// is at most half of a workgroup's share of the work. Order-balanced A/B on
+// one box, 64 packed sequences of 0 to 16 chunks, 80 heads (5,120 pairs):
+// one-chunk units 1509 us per pass, segments of 2: 1518, 4: 1417, 8: 1380,
+// 12: 1365, 16: 1420 (the same with slow decay: 1384, -, 1288, 1271, 1239,
+// 1271), outputs bit-identical. Fewer pairs keep one-chunk units, whose
+// chain of hand-offs overlaps the chunks of a sequence across workgroups.
+constexpr int kChainSegPacked = 12;
+constexpr int64_t kSegPackedMinPairs = 2 * 2 * 256;
+
 int chain_segment(const Args &a) {
-  if (a.N == 256 || a.varlen) return 1;
+  if (a.N == 256) return 1;
   // one-chunk units when they all fit the chip at once: there each unit's
   // latency is the whole time, and a longer chain of dependent links within a
   // workgroup would only lengthen it
   if ((int64_t)a.nc_max * a.H <= kDeepMaxUnits) return 1;
+  if (a.varlen) return (int64_t)a.nseq * a.H >= kSegPackedMinPairs ? kChainSegPacked : 1;
   return kChainSeg;
 }
 

@@ -469,7 +469,8 @@ def test_conv_rejects_tensor_on_another_device(name):
     (dict(batch=2, seqlen=8192, nheads=80), 4),            # 160 pairs of 32 chunks: segments of 4
     (dict(batch=4, seqlen=2048, nheads=24), 1),            # 768 units: all fit the chip at once
     (dict(batch=2, seqlen=16384, nheads=64, dstate=256, ngroups=8), 1),   # N = 256
-    (dict(batch=1, seqlen=137028, nheads=80, num_seqs=64), 1),            # packed sequences
+    (dict(batch=1, seqlen=137028, nheads=80, num_seqs=64), 12),           # packed: 5,120 pairs
+    (dict(batch=1, seqlen=137028, nheads=80, num_seqs=12), 1),            # packed: 960 pairs
     (dict(batch=8, seqlen=2048, nheads=80, flags=ssd.SSD_FLAG_UNFUSED), 0),  # no chained kernel
     (dict(batch=8, seqlen=2048, nheads=80, dtype=ssd.SSD_DTYPE_F32), 0),
 ])

@@ -53,12 +53,19 @@ SMALL = {
     # more than 768 work units: the chained kernel walks segments of
     # consecutive chunks per workgroup, the state passed in registers inside a
     # segment and through the ring between segments. Five chunks per sequence
-    # (segments of 2, 2 and 1 chunks), slow decay so that every carry shows,
-    # and packed sequences of 0 to 6 chunks with initial states.
+    # (segments of 2, 2 and 1 chunks), slow decay so that every carry shows.
     "seg-odd-chunks-h0": si.scaled(C[2], batch=2, seqlen=1100, nheads=80, seed=2030),
     "seg-slow-h0": si.scaled(S["S1"], batch=2, seqlen=1800, nheads=52, seed=2031),
+    # packed sequences of 0 to 6 chunks with initial states, more than 768
+    # units but fewer than 1,024 (sequence, head) pairs: one-chunk units
     "seg-varlen-slow": si.scaled(S["S3"], nheads=40, num_seqs=9, h0_std=0.1, seed=2032,
                                  seq_lens=(1, 600, 0, 257, 1300, 513, 40, 768, 1025)),
+    # packed input with 1,040 pairs: segments of up to 12 chunks, one
+    # sequence of 13 chunks (two segments, a hand-off between them), empty
+    # and one-token sequences, initial states, slow decay
+    "seg-varlen-long": si.scaled(S["S3"], nheads=80, num_seqs=13, h0_std=0.1, seed=2035,
+                                 seq_lens=(1, 600, 0, 257, 3300, 513, 40, 768, 1025, 2000, 5,
+                                           256, 100)),
     # eight or more groups: one-chunk units handed out from one queue per XCD,
     # each over whole groups (N = 256 dense; packed input at N = 128 with more
     # units than the chip holds), slow decay so that every carry shows
