@@ -33,16 +33,22 @@
 //     predecessor's state is late publishes its own aggregate (S_c and its
 //     decay) and rebuilds h_in from the nearest published state and the
 //     aggregates after it (the chunk maps compose associatively), so no unit
-//     waits for its predecessor's own wait;
-//   - dense problems with more units than that (kSeg): runs of consecutive
-//     chunks of one (sequence, head) with the state carried in registers,
-//     either segments of four chunks or, with at least one pair per resident
-//     workgroup, one balanced range of the (sequence, head, chunk) order per
-//     workgroup, so only range or segment boundaries go through memory;
-//   - everything else (packed input, N = 256): one chunk each.
+//     waits for its predecessor's own wait (a sequence's second chunk, whose
+//     predecessor never waits, waits plainly);
+//   - problems with more units than that (kSeg): runs of consecutive chunks
+//     of one (sequence, head) with the state carried in registers: dense
+//     input in segments of four chunks or, with at least one pair per
+//     resident workgroup, one balanced range of the (sequence, head, chunk)
+//     order per workgroup; packed input with at least two pairs per resident
+//     workgroup in segments of up to twelve chunks. Only range or segment
+//     boundaries go through memory;
+//   - everything else (N = 256, packed input with fewer pairs): one chunk
+//     each, from one queue per XCD over whole groups when the groups split
+//     evenly over the XCDs.
 //
-// Tickets from an atomic counter order the work units so that a unit's
-// predecessors took smaller tickets. A workgroup only ever waits on a
+// Tickets from an atomic counter (or from per-XCD queues, each taken in
+// order) order the work units so that a unit's predecessors took smaller
+// tickets. A workgroup only ever waits on a
 // smaller ticket, i.e. on one that is already running, and every unit
 // publishes without waiting on a larger one, so the chain cannot deadlock
 // whatever order the hardware dispatches in. Every wait is bounded by a
@@ -50,7 +56,8 @@
 // hanging (the outputs are then wrong).
 //
 // LDS holds only x (the operand both products read transposed) and h_in
-// (bf16), 52 KB at chunk 256, so three workgroups share a CU. Each wave owns
+// (bf16), 52 KB at chunk 256 and N = 128, so three one-chunk workgroups
+// share a CU (two of the deep, segment and N = 256 kernels, by registers). Each wave owns
 // whole 32-row output tiles, so the two 16-row halves of a tile share every
 // x and h_in read. x is staged through registers rather than copied
 // global->LDS directly: while such a copy is pending, every wait on a
