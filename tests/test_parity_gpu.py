@@ -66,6 +66,12 @@ SMALL = {
     "seg-varlen-long": si.scaled(S["S3"], nheads=80, num_seqs=13, h0_std=0.1, seed=2035,
                                  seq_lens=(1, 600, 0, 257, 3300, 513, 40, 768, 1025, 2000, 5,
                                            256, 100)),
+    # the same at chunk 128, N = 64, two groups, no initial state: a sequence
+    # of 14 chunks (segments of 12 and 2) and one of exactly 12
+    "seg-varlen-q128": si.scaled(S["S3"], nheads=80, ngroups=2, dstate=64, chunk=128,
+                                 num_seqs=13, h0_std=0.0, seed=2036,
+                                 seq_lens=(129, 0, 1700, 64, 385, 1, 900, 256, 127, 1536, 40,
+                                           700, 300)),
     # eight or more groups: one-chunk units handed out from one queue per XCD,
     # each over whole groups (N = 256 dense; packed input at N = 128 with more
     # units than the chip holds), slow decay so that every carry shows
