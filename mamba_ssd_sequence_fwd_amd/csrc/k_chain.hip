@@ -35,16 +35,15 @@
 //     aggregates after it (the chunk maps compose associatively), so no unit
 //     waits for its predecessor's own wait (a sequence's second chunk, whose
 //     predecessor never waits, waits plainly);
-//   - problems with more units than that (kSeg): runs of consecutive chunks
-//     of one (sequence, head) with the state carried in registers: dense
-//     input in segments of four chunks or, with at least one pair per
-//     resident workgroup, one balanced range of the (sequence, head, chunk)
-//     order per workgroup; packed input with at least two pairs per resident
+//   - problems with more units than that and many (sequence, head) pairs
+//     (kSeg): runs of consecutive chunks of one pair with the state carried
+//     in registers: dense input with at least one pair per resident
+//     workgroup in one balanced range of the (sequence, head, chunk) order
+//     per workgroup; packed input with at least two pairs per resident
 //     workgroup in segments of up to twelve chunks. Only range or segment
 //     boundaries go through memory;
-//   - everything else (N = 256, packed input with fewer pairs): one chunk
-//     each, from one queue per XCD over whole groups when the groups split
-//     evenly over the XCDs.
+//   - everything else (N = 256, fewer pairs): one chunk each, from one queue
+//     per XCD over whole groups when the groups split evenly over the XCDs.
 //
 // Tickets from an atomic counter (or from per-XCD queues, each taken in
 // order) order the work units so that a unit's predecessors took smaller
@@ -953,12 +952,20 @@ bool chain_path_supports(const Args &a) {
 // at three workgroups each.
 constexpr int64_t kDeepMaxUnits = 3 * 256;
 
-// Chunks per work unit for problems with more units than the chip holds at
-// once. Order-balanced A/B on one box, with whole-row y stores, the 2.7B-shaped
-// workload: units of 1, 2, 3 and 4 chunks within 3% of each other (163-170 us
-// per pass over two rounds), so the longest is taken: it moves the fewest
-// hand-off bytes (42 MB per launch against 294 MB for one-chunk units).
+// Chunks per work unit for dense problems with more units than the chip holds
+// at once and at least as many (sequence, head) pairs as it holds segment
+// workgroups (2 per CU on 256 CUs; these take balanced ranges when they have
+// two or more chunks per sequence). Order-balanced A/B on one box, with
+// whole-row y stores, the 2.7B-shaped workload: units of 1, 2, 3 and 4 chunks
+// within 3% of each other (163-170 us per pass over two rounds), so the
+// longest is taken: it moves the fewest hand-off bytes (42 MB per launch
+// against 294 MB for one-chunk units). With fewer pairs a segment's chunks
+// run one after another inside a workgroup and the sequences' chains
+// lengthen: segments of 4 against one-chunk units, order-balanced, 160 pairs
+// of 32 chunks: 292.8 -> 183.5 us per pass; 64 pairs of 128 chunks: 1000.3
+// -> 413.8 us; 384 pairs of 8 chunks: 141.1 -> 115.4 us (bit-identical).
 constexpr int kChainSeg = 4;
+constexpr int64_t kSegDenseMinPairs = 2 * 256;
 
 // Packed input: segments of up to 12 chunks when there are at least twice as
 // many (sequence, head) pairs as the chip holds segment workgroups (2 per CU
@@ -979,7 +986,7 @@ int chain_segment(const Args &a) {
   // workgroup would only lengthen it
   if ((int64_t)a.nc_max * a.H <= kDeepMaxUnits) return 1;
   if (a.varlen) return (int64_t)a.nseq * a.H >= kSegPackedMinPairs ? kChainSegPacked : 1;
-  return kChainSeg;
+  return (int64_t)a.nseq * a.H >= kSegDenseMinPairs ? kChainSeg : 1;
 }
 
 // Workgroups of the segment kernel that one CU holds (its registers).

@@ -466,7 +466,7 @@ def test_conv_rejects_tensor_on_another_device(name):
     # 640 (sequence, head) pairs of 8 chunks, at least the 512 workgroups that
     # 256 CUs hold: balanced ranges, each walking whole sequences of 8 chunks
     (dict(batch=8, seqlen=2048, nheads=80), 8),
-    (dict(batch=2, seqlen=8192, nheads=80), 4),            # 160 pairs of 32 chunks: segments of 4
+    (dict(batch=2, seqlen=8192, nheads=80), 1),            # 160 pairs of 32 chunks: one-chunk units
     (dict(batch=4, seqlen=2048, nheads=24), 1),            # 768 units: all fit the chip at once
     (dict(batch=2, seqlen=16384, nheads=64, dstate=256, ngroups=8), 1),   # N = 256
     (dict(batch=1, seqlen=137028, nheads=80, num_seqs=64), 12),           # packed: 5,120 pairs

@@ -50,10 +50,10 @@ SMALL = {
     # 11 packed sequences, two of them empty, lengths from 1 to 900 tokens
     "varlen-11-seqs": si.scaled(C[4], nheads=4, num_seqs=11, h0_std=0.1, seed=2029,
                                 seq_lens=(300, 0, 1, 700, 256, 257, 0, 40, 900, 5, 513)),
-    # more than 768 work units: the chained kernel walks segments of
-    # consecutive chunks per workgroup, the state passed in registers inside a
-    # segment and through the ring between segments. Five chunks per sequence
-    # (segments of 2, 2 and 1 chunks), slow decay so that every carry shows.
+    # more than 768 work units on fewer than 512 (sequence, head) pairs:
+    # one-chunk units handing the state over through the two-slot ring
+    # (three workgroups per CU), odd chunk counts, slow decay so that every
+    # carry shows.
     "seg-odd-chunks-h0": si.scaled(C[2], batch=2, seqlen=1100, nheads=80, seed=2030),
     "seg-slow-h0": si.scaled(S["S1"], batch=2, seqlen=1800, nheads=52, seed=2031),
     # packed sequences of 0 to 6 chunks with initial states, more than 768
