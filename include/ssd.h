@@ -169,13 +169,16 @@ ssd_status ssd_forward(const ssd_problem *prob, const void *x, const void *dt,
  * (held until the process ends; its address is looked up on the first call
  * on a device, with that device current). The current device must be the
  * stream's device. Nothing is allocated, freed or synchronised.
- * Returns SSD_ERR_WORKSPACE, before anything is enqueued, for problems whose
- * workspace (ssd_workspace_size) exceeds 64 MiB; use ssd_forward for those.
- * On the default bf16 path the state hand-off takes 64 KiB per (sequence,
- * head) at P = 64, N = 128 and the C B^T and B^T tiles about 136 KiB per
- * (chunk, group) at chunk 256, so the 2.7B-shaped batch (8 sequences of
- * 2048 tokens, 80 heads: about 51 MB) fits and the 64-sequence packed batch
- * does not.
+ * Where the default bf16 path would give its chained kernel one state slot
+ * and one aggregate per (chunk, head) (grids of up to 1536 one-chunk units)
+ * and those do not fit, it uses the two slots per (sequence, head) of larger
+ * grids instead, with the same outputs. Returns SSD_ERR_WORKSPACE, before
+ * anything is enqueued, for problems whose workspace still exceeds 64 MiB;
+ * use ssd_forward for those. On the default bf16 path the state hand-off
+ * takes 64 KiB per (sequence, head) at P = 64, N = 128 and the C B^T and B^T
+ * tiles about 136 KiB per (chunk, group) at chunk 256, so the 2.7B-shaped
+ * batch (8 sequences of 2048 tokens, 80 heads: about 51 MB) fits and the
+ * 64-sequence packed batch does not.
  * All calls on one GPU share its scratch area, and each pass clears what it
  * needs cleared itself: calls that may overlap on one GPU (on different
  * streams, or from several host threads) race and give wrong results; order

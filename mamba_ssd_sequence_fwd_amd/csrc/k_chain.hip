@@ -430,15 +430,16 @@ __device__ __forceinline__ int wait_status(const int32_t *st) {
 
 // kDeep: every B^T tile of step 2 is loaded up front instead of four steps
 // ahead, at two workgroups per CU instead of three (more registers), and
-// units publish aggregates (one state slot per chunk). When a problem has no
-// more work units than the chip holds at once, each workgroup's own latency
-// is the whole time and this wins (config-1 shapes: 66 -> 56 us, then 57.0
-// -> 51.2 us with aggregates; the same aggregates with three workgroups per
-// CU and four-step prefetch: 56.3 us); with many units per slot the third
-// workgroup per CU hides that latency better (the 2.7B shapes: equal; long
-// packed input: 13% slower), and aggregates there cost more than they save
-// (N = 256 long sequences: 592 -> 662 us), so the launcher picks it by grid
-// size.
+// units publish aggregates (one state slot per chunk). When a problem has
+// about as many work units as the chip holds at once, each workgroup's own
+// latency is most of the time and this wins (4 sequences x 24 heads x 8
+// chunks, 768 units: 66 -> 56 us, then 57.0 -> 51.2 us with aggregates; the
+// same aggregates with three workgroups per CU and four-step prefetch: 56.3
+// us; up to twice as many units it still wins, kDeepMaxUnits); with many
+// units per slot the third workgroup per CU hides that latency better (the
+// 2.7B shapes: equal; long packed input: 13% slower), and aggregates there
+// cost more than they save (N = 256 long sequences: 592 -> 662 us), so the
+// layout picks it by grid size.
 //
 // kSeg: a work unit is a segment of up to a.seg consecutive chunks of one
 // (sequence, head), walked in order by the same workgroup. Inside a segment
@@ -948,9 +949,17 @@ bool chain_path_supports(const Args &a) {
          (a.N == 64 || a.N == 128 || a.N == 256);
 }
 
-// Work units up to which the deep-prefetch kernel is used: what 256 CUs hold
-// at three workgroups each.
-constexpr int64_t kDeepMaxUnits = 3 * 256;
+// Work units that 256 CUs hold at once, three workgroups each.
+constexpr int64_t kResidentUnits = 3 * 256;
+
+// One-chunk units up to which the look-back kernel (deep prefetch, two
+// workgroups per CU) runs when the layout gives it its per-chunk slots.
+// Order-balanced A/B on one box against the plain-wait kernel, outputs
+// bit-identical: 1,024 units (2 x 8 chunks x 64 heads) 62.2 -> 58.4 us per
+// pass; 1,152 (36 pairs x 32 chunks) 98.8 -> 79.9; 1,280 (80 pairs x 16)
+// 75.6 -> 71.5; 1,536 even. Above that the plain wait is faster (4,096 to
+// 8,192 units).
+constexpr int64_t kDeepMaxUnits = 6 * 256;
 
 // Chunks per work unit for dense problems with more units than the chip holds
 // at once and at least as many (sequence, head) pairs as it holds segment
@@ -984,7 +993,7 @@ int chain_segment(const Args &a) {
   // one-chunk units when they all fit the chip at once: there each unit's
   // latency is the whole time, and a longer chain of dependent links within a
   // workgroup would only lengthen it
-  if ((int64_t)a.nc_max * a.H <= kDeepMaxUnits) return 1;
+  if ((int64_t)a.nc_max * a.H <= kResidentUnits) return 1;
   if (a.varlen) return (int64_t)a.nseq * a.H >= kSegPackedMinPairs ? kChainSegPacked : 1;
   return (int64_t)a.nseq * a.H >= kSegDenseMinPairs ? kChainSeg : 1;
 }
@@ -1019,11 +1028,12 @@ int64_t chain_units(const Args &a) {
 // each over whole groups, when there are at least 8 groups (with fewer,
 // every XCD would still need every chunk's tiles).
 bool chain_group_queues(const Args &a) {
-  return a.seg <= 1 && !chain_lookback(a) && a.G % kRangeQueues == 0 && a.H % kRangeQueues == 0;
+  return a.seg <= 1 && !a.agg && a.G % kRangeQueues == 0 && a.H % kRangeQueues == 0;
 }
 
-// Whether the launch takes the kDeep kernel, whose units publish aggregates
-// and the state leaving every chunk (one slot each).
+// Whether a problem's layout gives the chained kernel per-chunk state and
+// aggregate slots (Args::agg non-null), with which the launch takes the kDeep
+// kernel: its units publish aggregates and the state leaving every chunk.
 bool chain_lookback(const Args &a) {
   return a.N != 256 && a.seg <= 1 && chain_units(a) <= kDeepMaxUnits;
 }
@@ -1040,7 +1050,7 @@ static hipError_t launch_chain_nq(const Args &a, const void *cb, const void *bt,
                          dim3(64 * kChainWaves), 0, st, a, cbp, btp);
       return hipGetLastError();
     }
-    if (blocks <= kDeepMaxUnits) {
+    if (a.agg) {  // per-chunk slots (at most kDeepMaxUnits one-chunk units)
       hipLaunchKernelGGL((k_ssd_chain<N, Q, true, false>), dim3((unsigned)blocks),
                          dim3(64 * kChainWaves), 0, st, a, cbp, btp);
       return hipGetLastError();

@@ -88,7 +88,10 @@ Path path_of(const ssd_problem &p) {
   return ssd::chain_path_supports(a) ? kMfmaChain : kMfmaUnfused;
 }
 
-Layout make_layout(const ssd_problem &p) {
+// allow_look false: the chained kernel's compact layout (two state slots per
+// (sequence, head), plain waits) even where per-chunk look-back slots would
+// be chosen, for a workspace of fixed size.
+Layout make_layout(const ssd_problem &p, bool allow_look = true) {
   Layout L{};
   const int64_t Q = p.chunk_size;
   L.nc_max = p.num_seqs > 0 ? p.seqlen / Q + p.num_seqs
@@ -134,7 +137,7 @@ Layout make_layout(const ssd_problem &p) {
     a.nc_per = a.varlen ? 0 : (p.seqlen + p.chunk_size - 1) / p.chunk_size;
     a.nc_max = (int32_t)L.nc_max;
     L.seg = a.seg = ssd::chain_segment(a);
-    look = ssd::chain_lookback(a);
+    look = allow_look && ssd::chain_lookback(a);
   }
   const size_t state_bytes = (size_t)p.headdim * p.dstate * sizeof(float);
   const size_t per_chunk = (size_t)L.nc_max * p.nheads * state_bytes;
@@ -158,7 +161,8 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 ssd_status check_args(const ssd_problem *p, const void *x, const void *dt, const float *A,
                       const void *B, const void *C, const int32_t *cu_seqlens, const void *y,
                       const float *initial_state, const float *final_state,
-                      const void *workspace, size_t workspace_bytes) {
+                      const void *workspace, size_t workspace_bytes,
+                      bool allow_look = true) {
   ssd_status st = ssd_validate(p);
   if (st != SSD_OK) return st;
   const bool varlen = p->num_seqs > 0;
@@ -172,7 +176,7 @@ ssd_status check_args(const ssd_problem *p, const void *x, const void *dt, const
   if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
       !aligned16(initial_state) || !aligned16(final_state))
     return fail(SSD_ERR_INVALID_ARG, "x, B, C, y and the states must be 16-byte aligned");
-  const Layout L = make_layout(*p);
+  const Layout L = make_layout(*p, allow_look);
   if (!workspace || ((uintptr_t)workspace % kAlign) != 0)
     return fail(SSD_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
   if (workspace_bytes < L.total)
@@ -683,7 +687,10 @@ ssd_status ssd_forward_noalloc(const ssd_problem *p, const void *x, const void *
   g_detail.clear();
   ssd_status st = ssd_validate(p);
   if (st != SSD_OK) return st;
-  const Layout L = make_layout(*p);
+  // the compact chained layout when the look-back slots would not fit
+  Layout L = make_layout(*p);
+  const bool look = L.total <= kScratchBytes;
+  if (!look) L = make_layout(*p, false);
   if (L.total > kScratchBytes)
     return fail(SSD_ERR_WORKSPACE,
                 "the problem needs %zu bytes of workspace; the allocation-free entry point has "
@@ -693,7 +700,7 @@ ssd_status ssd_forward_noalloc(const ssd_problem *p, const void *x, const void *
   void *ws = scratch_for_current_device(&dev);
   if (!ws) return SSD_ERR_HIP;
   st = check_args(p, x, dt, A, B, C, cu_seqlens, y, initial_state, final_state, ws,
-                  kScratchBytes);
+                  kScratchBytes, look);
   if (st != SSD_OK) return st;
   const ssd::Args a = make_args(p, L, x, dt, A, B, C, D, initial_state, cu_seqlens, y,
                                 final_state, ws);

@@ -134,6 +134,17 @@ def test_workspace_layout_chain_counters(lib):
         assert ssd.workspace_layout(P(flags=flags)).chain_sync_words == 0
 
 
+def test_workspace_lookback_slots_up_to_1536_units(lib):
+    """One state slot and one aggregate per (chunk, head) on grids of up to
+    1536 one-chunk units (the look-back kernel), two state slots per
+    (sequence, head) above that."""
+    state = 64 * 128 * 4
+    look = ssd.workspace_size(P(seqlen=2048, nheads=96, ngroups=1))    # 2 x 8 x 96 = 1536
+    assert look >= 2 * 1536 * state
+    plain = ssd.workspace_size(P(seqlen=2048, nheads=100, ngroups=1))  # 1600 units
+    assert plain < 1600 * state and plain >= 2 * 2 * 100 * state
+
+
 def test_workspace_grows_with_problem(lib):
     a = ssd.workspace_size(P(seqlen=1000))
     b = ssd.workspace_size(P(seqlen=2000))

@@ -1,9 +1,12 @@
 """ssd_forward_noalloc (the entry point that allocates nothing, its workspace
 a fixed scratch area in device memory) against ssd_forward on the same
-inputs, through the C ABI: three calls in a row on one GPU, each smaller than
-the one before (the 2.7B-shaped batch, a smaller dense batch, packed
-sequences), so each finds the scratch area holding the previous call's
-contents. Same kernels, so the outputs must be bit-identical."""
+inputs, through the C ABI: four calls in a row on one GPU, each smaller than
+the one before (the 2.7B-shaped batch, a dense batch whose look-back slots do
+not fit the scratch area, a smaller dense batch, packed sequences), so each
+finds the scratch area holding the previous call's contents. The outputs
+must be bit-identical: the same kernels, or the chained kernel with plain
+waits against its look-back variant, which rebuilds a chunk's input state in
+the same order of operations as the plain chain."""
 import ctypes
 
 import pytest
@@ -34,7 +37,11 @@ def _noalloc(inp, w):
 
 
 def test_noalloc_matches_forward_on_shrinking_calls():
+    # 2 x 8 chunks x 64 heads: 1,024 one-chunk units, whose per-chunk state
+    # and aggregate slots (64 MiB) exceed the scratch area, so this entry
+    # point takes the two-slot layout where ssd_forward takes the look-back
     cases = [C[2],
+             si.scaled(C[2], batch=2, seqlen=2048, nheads=64, seed=7003),
              si.scaled(C[2], batch=2, seqlen=1100, nheads=24, seed=7001),
              si.scaled(si.STRESS["S3"], nheads=8, num_seqs=5, seq_lens=(300, 0, 900, 1, 257),
                        h0_std=0.1, seed=7002)]
