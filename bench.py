@@ -7,11 +7,13 @@ P 64, N 128, G 1, chunk 256, bf16 in / fp32 accumulate and states, random
 fp32 initial state). Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line with: whole-job tokens/s over K plain passes (HIP events
-around the loop only), per-kernel times from a second run of K passes with a
-HIP event after every kernel, the roofline of the dominant kernel (the
-method's algorithmic bytes or flops per launch / its mean event time, with
-the design's own intermediate bytes reported apart as overhead), and the fp64
-CPU oracle timed on this host (a reported baseline, not a target).
+around the loop only; before them W warm-up passes and --ramp-s seconds of
+untimed passes, so that the GPU's clocks have ramped up), per-kernel times
+from a second run of K passes with a HIP event after every kernel, the
+roofline of the dominant kernel (the method's algorithmic bytes or flops per
+launch / its mean event time, with the design's own intermediate bytes
+reported apart as overhead), and the fp64 CPU oracle timed on this host (a
+reported baseline, not a target).
 
     python bench.py [--steps K] [--warmup W] [--config 0..4] [--no-cpu-baseline]
 """
@@ -199,14 +201,31 @@ def evict_caches(buf):
     return torch.sum(buf)
 
 
+def clock_ramp(run, stream, seconds):
+    """Untimed calls of ``run`` for ``seconds`` of wall time, after the
+    warm-up calls: the GPU raises its clocks only under sustained load. On
+    one MI355X, the 2.7B-shaped workload after 10 warm-up passes: the next
+    100 passes ran at 163.8 us each, 20 more at 151.6, then 147.9, and from
+    about 40 ms of load on every batch at 142.5-143.8. Returns the calls run."""
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            run()
+        n += 16
+        stream.synchronize()
+    return n
+
+
 def time_launches(run, args, stream):
     """Time ``args.steps`` calls of ``run`` with HIP events on ``stream``:
     back to back (warm caches), or with ``args.cold`` each call after
-    evict_caches. ``args.warmup``
-    untimed calls first. Returns (ms per call, wall seconds of the timed
-    region)."""
+    evict_caches. ``args.warmup`` untimed calls first, then untimed calls for
+    ``args.ramp_s`` seconds (clock_ramp). Returns (ms per call, wall seconds
+    of the timed region, calls of the clock ramp)."""
     for _ in range(args.warmup):
         run()
+    ramp = clock_ramp(run, stream, args.ramp_s)
     dev = torch.device("cuda:0")
     evict = torch.zeros(COLD_EVICT_BYTES // 4, device=dev) if args.cold else None
     torch.cuda.synchronize()
@@ -229,7 +248,7 @@ def time_launches(run, args, stream):
             e1.record(stream)
             e1.synchronize()
             total_ms += e0.elapsed_time(e1)
-    return total_ms / args.steps, time.perf_counter() - t0
+    return total_ms / args.steps, time.perf_counter() - t0, ramp
 
 
 def bench_decode(args):
@@ -244,7 +263,7 @@ def bench_decode(args):
     A, D, state = inp["A"].to(dev), inp["D"].to(dev), inp["state"].to(dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
-    ms, wall = time_launches(lambda: ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream),
+    ms, wall, ramp = time_launches(lambda: ssd.step(x, dt, A, B, C, D, state, y=y, stream=stream),
                              args, stream)
     e = 2
     alg_bytes = batch * H * P * N * 4 * 2 + batch * (2 * H * P * e + H * e + 2 * G * N * e)
@@ -253,7 +272,8 @@ def bench_decode(args):
     out = {
         "metric": "SSD decode step tokens/s (one token per sequence, one layer)",
         "value": round(batch / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup, "ramp_passes": ramp,
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "decode-2.7b-b%d" % batch, "batch": batch, "nheads": H,
@@ -289,14 +309,15 @@ def bench_scan(args):
     stream = torch.cuda.current_stream(dev)
     run = lambda: ssd.selective_scan(d["x"], d["delta"], d["A"], d["B"], d["C"], d["D"], d["h0"],
                                      y=y, final_state=hT, stream=stream)
-    ms, wall = time_launches(run, args, stream)
+    ms, wall, ramp = time_launches(run, args, stream)
     elems = batch * L * Dm * N
     alg_bytes = batch * L * (3 * Dm * 2 + 2 * N * 2) + Dm * N * 4 + 2 * batch * Dm * N * 4
     achieved = elems / (ms * 1e-3)
     out = {
         "metric": "Mamba-1 selective scan tokens/s (the SSD layer's comparator)",
         "value": round(batch * L / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup, "ramp_passes": ramp,
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "mamba1-scan-2.7b-N%d" % N, "batch": batch, "seq_len": L,
@@ -367,6 +388,7 @@ def bench_backward(args):
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         plan.run(stream)
+    ramp = clock_ramp(lambda: plan.run(stream), stream, args.ramp_s)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     times = plan.run_timed(args.steps, stream)
@@ -402,7 +424,8 @@ def bench_backward(args):
         "metric": "SSD backward tokens/s (gradients of x, dt, A, B, C, D, h0; states "
                   "recomputed)",
         "value": round(plan.tokens / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "ramp_passes": ramp,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "bwd-" + w.name, "batch": w.batch if not w.num_seqs else 1,
@@ -433,7 +456,7 @@ def bench_conv(args):
     C = torch.empty_like(B)
     ho = torch.empty_like(hist)
     stream = torch.cuda.current_stream(dev)
-    ms, wall = time_launches(lambda: ssd.conv1d_silu(xbc, w, b, x_dim, bc_dim, hist, x=x, B=B,
+    ms, wall, ramp = time_launches(lambda: ssd.conv1d_silu(xbc, w, b, x_dim, bc_dim, hist, x=x, B=B,
                                                      C=C, history_out=ho, stream=stream),
                              args, stream)
     T, e = batch * L, 2
@@ -443,7 +466,8 @@ def bench_conv(args):
     out = {
         "metric": "SSD conv front tokens/s (causal depthwise conv1d + SiLU producing x, B, C)",
         "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup, "ramp_passes": ramp,
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": workload, "batch": batch, "seq_len": L, "x_dim": x_dim,
@@ -464,6 +488,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--ramp-s", type=float, default=0.3,
+                    help="after the warm-up, untimed passes for this many seconds, so that "
+                         "the GPU's clocks have ramped up under load before the timed region")
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
@@ -548,11 +575,12 @@ def main():
                     per_sequence=args.per_sequence)
     stream = torch.cuda.current_stream(dev)
 
-    # Timed region (after W untimed warm-up passes): K plain ssd_forward passes (exactly what a caller
-    # enqueues), HIP events on the kernels' stream around the whole loop only,
-    # synchronised on both sides (or, with --cold, one pass at a time after an
-    # eviction read that the events do not cover).
-    ms_per_step, wall = time_launches(lambda: plan.run(stream), args, stream)
+    # Timed region (after W untimed warm-up passes and the clock ramp): K plain
+    # ssd_forward passes (exactly what a caller enqueues), HIP events on the
+    # kernels' stream around the whole loop only, synchronised on both sides
+    # (or, with --cold, one pass at a time after an eviction read that the
+    # events do not cover).
+    ms_per_step, wall, ramp = time_launches(lambda: plan.run(stream), args, stream)
     if plan.chain_error():
         print("bench.py: a chained workgroup timed out waiting for its predecessor's state; "
               "the outputs of the timed passes are invalid", file=sys.stderr)
@@ -606,7 +634,8 @@ def main():
     path = cost["_path"]
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "ramp_passes": ramp,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "fp32", "data": "synthetic",
         "config": {"workload": w.name, "kernels": ("unfused" if args.unfused else
