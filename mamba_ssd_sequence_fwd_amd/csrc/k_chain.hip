@@ -339,6 +339,10 @@ __host__ __device__ inline int64_t chain_grid(const Args &a) {
   return (int64_t)(a.varlen ? a.nc_max : a.nseq * a.nc_per) * a.H;
 }
 
+// First head of XCD queue q (of kRangeQueues) over H heads: contiguous
+// ranges whose sizes differ by at most one.
+__host__ __device__ inline int head_lo(int H, int q) { return (int)((int64_t)H * q / kRangeQueues); }
+
 // Per-(chunk, head) state slots in the workspace (the state leaving a chunk,
 // and a chunk's aggregate), in the state-tile layout of the waves (tile (j,
 // pt) of wave w: rows n = 16 (w NTW + j) + 4(lane/16) + r, column p = 16 pt
@@ -480,7 +484,7 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
   __shared__ __attribute__((aligned(16))) float sU[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];
   __shared__ float sTot[4];
-  __shared__ int sTicket, sReady, sNb;
+  __shared__ int sTicket, sQueue, sReady, sNb;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -501,25 +505,30 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
       int got = -1;
       for (int d = 0; d < kRangeQueues && got < 0; ++d) {
         const int q = (int)((x + d) % kRangeQueues);
-        const int t = atomicAdd(a.sync + kRangeQueueWord + q, 1);
+        const int t = atomicAdd(a.sync + kRangeQueueWord + q * kQueueStride, 1);
         if (t < per) got = q * per + t;
       }
       sTicket = got;
-    } else if (!kSeg && !kDeep && a.gqueue) {
-      // one queue per XCD over an eighth of the heads (whole groups), taken
-      // in chunk order: the workgroups sharing an L2 read the same group's
-      // B^T and C B^T tiles, and a unit's predecessor (same head) comes
-      // earlier from the same queue
+    } else if (!kSeg && a.gqueue) {
+      // one queue per XCD over a contiguous eighth of the heads (whole groups
+      // when they split evenly), taken in chunk order: the workgroups sharing
+      // an L2 read the same groups' B^T and C B^T tiles, eight counters take
+      // the atomics one counter took, and a unit's predecessor (same head)
+      // comes earlier from the same queue. An XCD whose queue is used up
+      // takes from the next ones.
       unsigned x;
       asm volatile("s_getreg_b32 %0, hwreg(20, 0, 4)" : "=s"(x));  // XCC_ID
-      const int per = (int)(chain_grid(a) / kRangeQueues);
-      int got = -1;
+      const int64_t per_head = chain_grid(a) / a.H;  // units of one head
+      int got = -1, gq = 0;
       for (int d = 0; d < kRangeQueues && got < 0; ++d) {
         const int q = (int)((x + d) % kRangeQueues);
-        const int t = atomicAdd(a.sync + kRangeQueueWord + q, 1);
-        if (t < per) got = q * per + t;
+        const int64_t cap = per_head * (head_lo(a.H, q + 1) - head_lo(a.H, q));
+        if (cap == 0) continue;
+        const int t = atomicAdd(a.sync + kRangeQueueWord + q * kQueueStride, 1);
+        if (t < cap) got = t, gq = q;
       }
       sTicket = got;
+      sQueue = gq;
     } else {
       sTicket = atomicAdd(ticket, 1);
     }
@@ -536,17 +545,16 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
     const int64_t u0 = p0 * a.nc_per, units = (p1 - p0) * a.nc_per;
     rlo = u0 + t * units / per;
     rhi = u0 + (t + 1) * units / per;
-  } else if (!kSeg && !kDeep && a.gqueue) {
+  } else if (!kSeg && a.gqueue) {
     if (tk < 0) return;  // (every workgroup finds a unit: as many units as workgroups)
-    const int per = (int)(chain_grid(a) / kRangeQueues), q = tk / per, t = tk - q * per;
-    const int hq = a.H / kRangeQueues;
+    const int q = sQueue, hl = head_lo(a.H, q), hq = head_lo(a.H, q + 1) - hl, t = tk;
     if (!a.varlen) {
       const int j = t / (a.nseq * hq), r = t - j * (a.nseq * hq), s = r / hq;
-      h = q * hq + (r - s * hq);
+      h = hl + (r - s * hq);
       c0 = s * a.nc_per + j;
     } else {
       const int kk = t / hq;
-      h = q * hq + (t - kk * hq);
+      h = hl + (t - kk * hq);
       if (kk >= a.plan[0]) return;  // unused slot: uniform per workgroup
       c0 = a.plan[a.order_off + kk];
     }
@@ -1024,12 +1032,19 @@ int64_t chain_units(const Args &a) {
   return (((int64_t)a.nc_max + (int64_t)a.nseq * (s - 1)) / s) * a.H;
 }
 
-// One-chunk units on large grids take their units from one queue per XCD,
-// each over whole groups, when there are at least 8 groups (with fewer,
-// every XCD would still need every chunk's tiles).
-bool chain_group_queues(const Args &a) {
-  return a.seg <= 1 && !a.agg && a.G % kRangeQueues == 0 && a.H % kRangeQueues == 0;
-}
+// One-chunk units take their units from one queue per XCD, each over a
+// contiguous eighth of the heads (whole groups when there are at least 8 and
+// they split evenly), where one ticket counter served grids with fewer
+// groups. The ticket is the first thing every workgroup waits for: a
+// timing-only copy that took the grid's block order as the ticket ran 4 x 8
+// chunks x 24 heads (look-back kernel) at 45.8 us per pass against 50.1, and
+// one that took the ticket but used the block order at 50.0. Order-balanced
+// A/B on one box, outputs bit-identical, per pass: eight queues against the
+// one counter, their counters packed in one line: 51.5 against 50.5, 2 x 8
+// x 64 heads 56.5 against 55.9, 2 x 32 x 64 heads (plain wait) 156.9 against
+// 161.9; with the counters 256 bytes apart (kQueueStride): 51.0 -> 47.7,
+// 56.9 -> 53.0, 152.4 -> 148.1.
+bool chain_group_queues(const Args &a) { return a.seg <= 1; }
 
 // Whether a problem's layout gives the chained kernel per-chunk state and
 // aggregate slots (Args::agg non-null), with which the launch takes the kDeep

@@ -119,17 +119,18 @@ def test_workspace_layout_varlen_bound(lib):
 
 def test_workspace_layout_chain_counters(lib):
     """The default bf16 path (chained workgroups) has a status word and a
-    decay word per (chunk, head) after a 64-word header, then the state
+    decay word per (chunk, head) after a 576-word header (ticket, error word
+    and eight queue counters 64 words apart), then the state
     leaving every chunk and (one-chunk units) every chunk's aggregate, fp32
     P x N each; the other paths have none."""
     lay = ssd.workspace_layout(P())
     nc = 2 * 4                                   # batch 2, ceil(1000/256) = 4
-    assert lay.chain_sync_words == 64 + 2 * nc * 8 and lay.chain_sync % 256 == 0
+    assert lay.chain_sync_words == 576 + 2 * nc * 8 and lay.chain_sync % 256 == 0
     assert lay.chain_chunks_per_unit == 1        # 64 units: one chunk each, aggregates kept
     assert ssd.workspace_size(P()) >= lay.chain_sync + 4 * lay.chain_sync_words + \
         2 * nc * 8 * 64 * 128 * 4
     lay_v = ssd.workspace_layout(P(batch=1, seqlen=5000, num_seqs=7))
-    assert lay_v.chain_sync_words == 64 + 2 * (5000 // 256 + 7) * 8
+    assert lay_v.chain_sync_words == 576 + 2 * (5000 // 256 + 7) * 8
     for flags in (ssd.SSD_FLAG_UNFUSED, ssd.SSD_FLAG_PER_SEQUENCE, ssd.SSD_FLAG_GENERIC_KERNELS):
         assert ssd.workspace_layout(P(flags=flags)).chain_sync_words == 0
 
