@@ -29,12 +29,12 @@
 //      (the chunk_scan step); y.
 //
 // Work units, chosen by the launcher from the grid size:
-//   - problems the chip holds at once (kDeep): one chunk each; a unit whose
-//     predecessor's state is late publishes its own aggregate (S_c and its
-//     decay) and rebuilds h_in from the nearest published state and the
-//     aggregates after it (the chunk maps compose associatively), so no unit
-//     waits for its predecessor's own wait (a sequence's second chunk, whose
-//     predecessor never waits, waits plainly);
+//   - problems of up to about twice what the chip holds at once (kDeep):
+//     one chunk each; a unit whose predecessor's state is late publishes its
+//     own aggregate (S_c and its decay) and rebuilds h_in from the nearest
+//     published state and the aggregates after it (the chunk maps compose
+//     associatively), so no unit waits for its predecessor's own wait (a
+//     sequence's second chunk, whose predecessor never waits, waits plainly);
 //   - problems with more units than that and many (sequence, head) pairs
 //     (kSeg): runs of consecutive chunks of one pair with the state carried
 //     in registers: dense input with at least one pair per resident
@@ -42,15 +42,17 @@
 //     per workgroup; packed input with at least two pairs per resident
 //     workgroup in segments of up to twelve chunks. Only range or segment
 //     boundaries go through memory;
-//   - everything else (N = 256, fewer pairs): one chunk each, from one queue
-//     per XCD over whole groups when the groups split evenly over the XCDs.
+//   - everything else (N = 256, fewer pairs): one chunk each.
+// One-chunk units and ranges come from one queue per XCD (one-chunk units:
+// over a contiguous eighth of the heads, whole groups where they split
+// evenly), segments from one counter.
 //
-// Tickets from an atomic counter (or from per-XCD queues, each taken in
-// order) order the work units so that a unit's predecessors took smaller
-// tickets. A workgroup only ever waits on a
-// smaller ticket, i.e. on one that is already running, and every unit
-// publishes without waiting on a larger one, so the chain cannot deadlock
-// whatever order the hardware dispatches in. Every wait is bounded by a
+// Tickets from these counters, each taken in order, order the work units so
+// that a unit's predecessors took smaller tickets of the same queue. A
+// workgroup only ever waits on a smaller ticket, i.e. on one that is
+// already running, and every unit publishes without waiting on a larger
+// one, so the chain cannot deadlock whatever order the hardware dispatches
+// in. Every wait is bounded by a
 // wall-clock limit; a wait that runs out sets an error word instead of
 // hanging (the outputs are then wrong).
 //
