@@ -129,8 +129,8 @@ __attribute__((amdgpu_waves_per_eu(N == 256 ? 2 : 3))) void k_chunk_state_mfma(A
 // bf16, tile pair = i (i + 1) / 2 + j, half u = rows 16u..16u+15 of tile i.
 // Two launch shapes, one wave per block:
 //   PAIRWISE: one wave per (chunk, group, tile pair), every load issued at
-//     once -- for small problems, where the grid would otherwise not fill
-//     the GPU;
+//     once, and on the chain path one wave per (chunk, group, B^T step) --
+//     for small problems, where the grid would otherwise not fill the GPU;
 //   otherwise: one wave per (chunk, group, {i, T-1-i}), T+1 tile pairs each,
 //     C rows loaded once per row tile.
 // On the chain path the same kernel writes B^T in the A-operand layout of the
@@ -221,6 +221,10 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
   bf16 *btb =
       a.bt ? static_cast<bf16 *>(a.bt) + ((size_t)c * a.G + g) * (N / 16) * T * 512 : nullptr;
   if (PAIRWISE) {
+    if ((int)blockIdx.z >= PAIRS) {  // chain path: one wave per B^T step
+      bt_step<N>(B, ldr, k.len, (int)blockIdx.z - PAIRS, T, btb, sBt);
+      return;
+    }
     const int pair = blockIdx.z;
     int i = 0;
     while ((i + 1) * (i + 2) / 2 <= pair) ++i;
@@ -232,7 +236,6 @@ __global__ __launch_bounds__(64) void k_chunk_cb(Args a, bf16 *cb) {
       for (int ks = 0; ks < KS; ++ks)
         cop[u][ks] = ldg8_row(C, ldr, 32 * i + 16 * u + lr, k.len, 32 * ks + 8 * lg);
     cb_pair<N>(B, ldr, k.len, j, cop, base + (size_t)pair * 2 * 512);
-    if (btb && j == i) bt_step<N>(B, ldr, k.len, i, T, btb, sBt);
   } else {
     const int w = blockIdx.z;
 #pragma unroll 1
@@ -421,11 +424,13 @@ static hipError_t launch_nq(const Args &a, bf16 *cb, hipStream_t st, int which) 
     hipLaunchKernelGGL((k_chunk_state_mfma<N, Q, true>), dim3(a.nc_max, a.H), dim3(256), 0, st,
                        a);
   } else if (which == 1) {
-    // Small problems: one wave per tile pair, so the grid fills the GPU.
+    // Small problems: one wave per tile pair, and on the chain path one more
+    // per B^T step, so the grid fills the GPU and no wave does both.
     constexpr int T = Q / 32;
     if ((int64_t)a.nc_max * a.G <= 256)
-      hipLaunchKernelGGL((k_chunk_cb<N, Q, true>), dim3(a.nc_max, a.G, T * (T + 1) / 2),
-                         dim3(64), 0, st, a, cb);
+      hipLaunchKernelGGL((k_chunk_cb<N, Q, true>),
+                         dim3(a.nc_max, a.G, T * (T + 1) / 2 + (a.bt ? T : 0)), dim3(64), 0,
+                         st, a, cb);
     else if (Q >= 128)
       hipLaunchKernelGGL((k_chunk_cb_staged<N, (Q >= 128 ? Q : 128)>), dim3(a.nc_max, a.G),
                          dim3(256), 0, st, a, cb);
