@@ -374,9 +374,10 @@ def backward_cost(w: si.Workload, inp: dict) -> dict:
 
 def bench_backward(args):
     """Backward pass of the SSD layer on a workload config: K back-to-back
-    ssd_backward calls with a HIP event after every kernel, on the stream the
-    kernels run on. The states are recomputed inside (no forward output is
-    read)."""
+    plain ssd_backward calls timed with HIP events around the K calls, on the
+    stream the kernels run on; after the timed region, K more calls with a HIP
+    event after every kernel give the per-kernel times. The states are
+    recomputed inside (no forward output is read)."""
     w = si.CONFIGS[args.config]
     inp = si.make_inputs(w)
     gin = si.make_grad_inputs(w, inp)
@@ -386,17 +387,9 @@ def bench_backward(args):
     plan = ssd.BackwardPlan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
                             gin["dy"].to(dev), gin["dhT"].to(dev), w.chunk, inp["cu_seqlens"])
     stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        plan.run(stream)
-    ramp = clock_ramp(lambda: plan.run(stream), stream, args.ramp_s)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    times = plan.run_timed(args.steps, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_kernel_ms = times.as_dict()
-    total_ms = per_kernel_ms.pop("_total_ms")
-    ms_per_step = total_ms / args.steps
+    ms_per_step, wall, ramp = time_launches(lambda: plan.run(stream), args, stream)
+    per_kernel_ms = plan.run_timed(args.steps, stream).as_dict()
+    per_kernel_ms.pop("_total_ms")
     cost = backward_cost(w, inp)
     kernels = {}
     for name, ms in per_kernel_ms.items():
