@@ -468,7 +468,11 @@ __device__ __forceinline__ int wait_status(const int32_t *st) {
 // last part first (it starts at a pair's first chunk and waits on nothing),
 // then the whole pairs, then the first part, whose predecessor the workgroup
 // of the previous range (taken earlier from the same queue) walked first.
-template <int N, int Q, bool kDeep, bool kSeg>
+// kStreamX (segments of packed input): x is loaded with the nontemporal
+// hint, so that the rows every unit reads once do not push the B, C and
+// C B^T tiles that all heads share out of the L2 (there every XCD walks
+// every sequence's chunks). Dense grids keep plain loads, which wait less.
+template <int N, int Q, bool kDeep, bool kSeg, bool kStreamX = false>
 __global__ __launch_bounds__(64 * kChainWaves)
 __attribute__((amdgpu_waves_per_eu(N == 256 || kDeep || kSeg ? 2 : 3,
                                    N == 256 || kDeep || kSeg ? 2 : 3)))
@@ -597,8 +601,12 @@ void k_ssd_chain(Args a, const bf16 *cb, const bf16 *bt) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const int r = 32 * ks + 8 * wave + (lane >> 3);
-      dst[ks] = *reinterpret_cast<const bf16x8 *>(
+      const bf16x8 *src = reinterpret_cast<const bf16x8 *>(
           xb + (uint32_t)min(r, len - 1) * (uint32_t)(ldx * 2) + 16u * (uint32_t)(lane & 7));
+      if constexpr (kStreamX)
+        dst[ks] = __builtin_nontemporal_load(src);
+      else
+        dst[ks] = *src;
     }
   };
 
@@ -1063,8 +1071,12 @@ static hipError_t launch_chain_nq(const Args &a, const void *cb, const void *bt,
   const bf16 *cbp = static_cast<const bf16 *>(cb), *btp = static_cast<const bf16 *>(bt);
   if constexpr (N != 256) {  // at N = 256 neither variant fits the registers
     if (a.seg > 1) {
-      hipLaunchKernelGGL((k_ssd_chain<N, Q, false, true>), dim3((unsigned)blocks),
-                         dim3(64 * kChainWaves), 0, st, a, cbp, btp);
+      if (a.varlen)
+        hipLaunchKernelGGL((k_ssd_chain<N, Q, false, true, true>), dim3((unsigned)blocks),
+                           dim3(64 * kChainWaves), 0, st, a, cbp, btp);
+      else
+        hipLaunchKernelGGL((k_ssd_chain<N, Q, false, true>), dim3((unsigned)blocks),
+                           dim3(64 * kChainWaves), 0, st, a, cbp, btp);
       return hipGetLastError();
     }
     if (a.agg) {  // per-chunk slots (at most kDeepMaxUnits one-chunk units)
